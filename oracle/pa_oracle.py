@@ -1,0 +1,255 @@
+"""Plain CPU oracle for paged KV-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product
+package (``paged_kv_cache_167_amd``) never imports it, and the two share no
+code: no kernels, headers, helpers, tables or pre/post-processing.  The only
+thing both sides consume is the seeded synthetic input from ``workloads/``,
+which contains none of the arithmetic below.
+
+Everything here is numpy, float64 for all floating point.  It is slow and
+written to be checked against the pages by eye.
+
+Sources (page title, section):
+  [DRV]  "揭开 NVIDIA 驱动栈的面纱：GPU 显存页表与 vLLM 中的 PagedAttention
+         是如何在底层协同的" (kwkd.cn) -- section 6 gives the logical-token to
+         (physical block, offset) translation with a worked example, and the
+         k_cache pointer formula.
+  [SRC]  vLLM source walk-through page (peacm.com) -- section 3.2 shows the
+         append of a new token into the last block, section 3.4 the per-block
+         paged attention loop, the tail mask and the online-softmax update.
+  [CON]  "PagedAttention：当 KV Cache 遇到操作系统分页" (forceinjection.github.io)
+         -- section 3.1 (block = B tokens of one layer; block table maps logical
+         to physical blocks), section 3.2 (the kernel walks the table and
+         gathers block by block).
+  [SOSP] "《Efficient Memory Management for LLM Serving with PagedAttention》
+         深度解读报告" (zako-mio.github.io) -- section 2.3 (K and V blocks are
+         managed separately; the fill count keeps padding out of the result),
+         section 3.3 (the result equals the one on contiguously stored KV),
+         section 3.4 (write the new token first, then attend over all valid KV),
+         section 4.4 (the attention mathematics is unchanged).
+
+Readings where the pages are silent (each listed in the design notes):
+  * slot encoding: slot = physical_block * B + offset; slot < 0 means "skip".
+  * GQA: query head h reads kv head h // G, G = num_q_heads / num_kv_heads.
+  * context_lens count the token just written (write first, then attend).
+  * ctx == 0 yields an all-zero output row.
+  * pool layout [num_blocks, num_kv_heads, B, head_dim], K and V separate.
+
+Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
+(worked example from [DRV] section 6, brute force, torch SDPA on contiguous
+K/V, permutation / block-size / sharing invariants, closed forms).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Address translation  ([DRV] section 6; [CON] section 3.1)
+# ---------------------------------------------------------------------------
+
+def locate_kv(logical_pos: int, block_table, block_size: int) -> tuple[int, int]:
+    """Map a logical token position to (physical block id, offset in block).
+
+    The logical block is the position divided by the block size, the offset is
+    the remainder, and the block table turns the logical block into the
+    physical one ([DRV] section 6; [SRC] section 3.2 does the same split when
+    appending a token).
+    """
+    logical_block = logical_pos // block_size
+    offset = logical_pos % block_size
+    return int(block_table[logical_block]), int(offset)
+
+
+def slot_to_block_offset(slot: int, block_size: int) -> tuple[int, int]:
+    """Decode the flat slot index (reading: slot = phys * B + offset)."""
+    return int(slot) // block_size, int(slot) % block_size
+
+
+# ---------------------------------------------------------------------------
+# Cache write  ([SRC] section 3.2 append_token; [SOSP] sections 3.2 and 3.4)
+# ---------------------------------------------------------------------------
+
+def cache_write(k, v, slot_mapping, k_cache, v_cache, block_size: int):
+    """Return copies of the two pools with each new token's K/V stored in its slot.
+
+    k, v:          [T, Hkv, D]
+    slot_mapping:  [T] integers, slot = phys * B + offset; negative = skip
+    k_cache/v_cache: [N, Hkv, B, D], same dtype as k/v
+
+    The store is a plain element copy in the cache dtype (no arithmetic), so
+    the result is bit-exact by construction.  K and V are separate pools
+    ([SOSP] section 2.3).
+    """
+    kc = np.array(k_cache, copy=True)
+    vc = np.array(v_cache, copy=True)
+    for t in range(len(slot_mapping)):
+        slot = int(slot_mapping[t])
+        if slot < 0:
+            continue
+        blk, off = slot_to_block_offset(slot, block_size)
+        kc[blk, :, off, :] = k[t]  # every kv head of token t
+        vc[blk, :, off, :] = v[t]
+    return kc, vc
+
+
+# ---------------------------------------------------------------------------
+# Gather through the block table  ([CON] section 3.2; [SOSP] section 2.3)
+# ---------------------------------------------------------------------------
+
+def gather_head(cache, table_row, ctx: int, block_size: int, kv_head: int) -> np.ndarray:
+    """Collect one kv head of one sequence into a contiguous [ctx, D] float64 array.
+
+    Logical blocks 0..ceil(ctx/B)-1 are looked up in the table in order, their
+    [B, D] tiles are concatenated, and only the first ctx positions are kept:
+    the unfilled tail of the last block never enters the result ([SOSP]
+    section 2.3; [SRC] section 3.4 masks the same positions).
+    """
+    n_blocks = -(-ctx // block_size)
+    tiles = [np.asarray(cache[int(table_row[j]), kv_head], dtype=np.float64)
+             for j in range(n_blocks)]
+    if not tiles:
+        return np.zeros((0, cache.shape[-1]), dtype=np.float64)
+    return np.concatenate(tiles, axis=0)[:ctx]
+
+
+# ---------------------------------------------------------------------------
+# Decode attention: the plain definition  ([SOSP] sections 3.3 and 4.4)
+# ---------------------------------------------------------------------------
+
+def softmax(z: np.ndarray) -> np.ndarray:
+    """Textbook softmax with the max subtracted ([SRC] section 3.4, 'traditional' form)."""
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def decode_one(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+               block_size: int, num_kv_heads: int, s: int, h: int) -> np.ndarray:
+    """Attention output of query head h of sequence s, float64 [D].
+
+    Paged attention computes exactly the attention over the contiguously
+    stored KV ([SOSP] sections 3.3, 4.4), so this is that definition:
+    out = softmax(scale * K q) V over the sequence's first ctx positions.
+    """
+    num_q_heads = q.shape[1]
+    group = num_q_heads // num_kv_heads
+    kv_head = h // group
+    ctx = int(context_lens[s])
+    d = q.shape[2]
+    if ctx == 0:
+        return np.zeros(d, dtype=np.float64)
+    keys = gather_head(k_cache, block_tables[s], ctx, block_size, kv_head)
+    vals = gather_head(v_cache, block_tables[s], ctx, block_size, kv_head)
+    qv = np.asarray(q[s, h], dtype=np.float64)
+    p = softmax(float(scale) * (keys @ qv))
+    return p @ vals
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+           block_size: int, num_kv_heads: int) -> np.ndarray:
+    """All outputs, float64 [S, Hq, D]; one gather per (sequence, kv head)."""
+    num_seqs, num_q_heads, d = q.shape
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((num_seqs, num_q_heads, d), dtype=np.float64)
+    for s in range(num_seqs):
+        ctx = int(context_lens[s])
+        if ctx == 0:
+            continue
+        for kvh in range(num_kv_heads):
+            keys = gather_head(k_cache, block_tables[s], ctx, block_size, kvh)
+            vals = gather_head(v_cache, block_tables[s], ctx, block_size, kvh)
+            for g in range(group):
+                h = kvh * group + g
+                qv = np.asarray(q[s, h], dtype=np.float64)
+                p = softmax(float(scale) * (keys @ qv))
+                out[s, h] = p @ vals
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Algebra the GPU path relies on, written as plain mirrors so the tests can pin
+# them to the definition above.  Neither is used to produce expected values for
+# the GPU comparison; those come from decode()/decode_one().
+# ---------------------------------------------------------------------------
+
+def decode_one_online(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                      block_size: int, num_kv_heads: int, s: int, h: int) -> np.ndarray:
+    """Block-by-block online softmax ([SRC] section 3.4, the running max / sum update).
+
+    Per logical block: new max = max(old max, block max); correction =
+    exp(old max - new max); running sum = old sum * correction + sum of
+    exp(score - new max) over the block; running output likewise; divide by
+    the running sum at the end.  The page's code snippet has defects (an
+    undefined previous max, a final division by the output's own sum); the
+    recurrence stated beside it is what is followed here.
+    """
+    num_q_heads = q.shape[1]
+    group = num_q_heads // num_kv_heads
+    kv_head = h // group
+    ctx = int(context_lens[s])
+    d = q.shape[2]
+    if ctx == 0:
+        return np.zeros(d, dtype=np.float64)
+    qv = np.asarray(q[s, h], dtype=np.float64)
+    m = -math.inf
+    ell = 0.0
+    acc = np.zeros(d, dtype=np.float64)
+    n_blocks = -(-ctx // block_size)
+    for j in range(n_blocks):
+        phys = int(block_tables[s][j])
+        valid = min(block_size, ctx - j * block_size)
+        kb = np.asarray(k_cache[phys, kv_head, :valid], dtype=np.float64)
+        vb = np.asarray(v_cache[phys, kv_head, :valid], dtype=np.float64)
+        z = float(scale) * (kb @ qv)
+        m_new = max(m, float(z.max()))
+        corr = math.exp(m - m_new) if m != -math.inf else 0.0
+        e = np.exp(z - m_new)
+        ell = ell * corr + float(e.sum())
+        acc = acc * corr + e @ vb
+        m = m_new
+    return acc / ell
+
+
+def decode_one_partitioned(q, k_cache, v_cache, block_tables, context_lens, scale: float,
+                           block_size: int, num_kv_heads: int, s: int, h: int,
+                           partition_size: int) -> np.ndarray:
+    """Split the context into partitions, normalise each, merge by log-sum-exp.
+
+    Not on the pages: it is the online-softmax merge of [SRC] section 3.4
+    applied to whole partitions instead of blocks.  Partition p covers logical
+    positions [p*P, min((p+1)*P, ctx)); it yields its max m_p, its sum l_p and
+    its normalised output o_p.  The merge takes M = max m_p, weights
+    w_p = l_p * exp(m_p - M), and returns sum(w_p o_p) / sum(w_p), adding
+    partitions in index order.
+    """
+    num_q_heads = q.shape[1]
+    group = num_q_heads // num_kv_heads
+    kv_head = h // group
+    ctx = int(context_lens[s])
+    d = q.shape[2]
+    if ctx == 0:
+        return np.zeros(d, dtype=np.float64)
+    keys = gather_head(k_cache, block_tables[s], ctx, block_size, kv_head)
+    vals = gather_head(v_cache, block_tables[s], ctx, block_size, kv_head)
+    qv = np.asarray(q[s, h], dtype=np.float64)
+    z = float(scale) * (keys @ qv)
+    parts = []
+    for start in range(0, ctx, partition_size):
+        zp = z[start:start + partition_size]
+        m_p = float(zp.max())
+        e = np.exp(zp - m_p)
+        l_p = float(e.sum())
+        o_p = (e @ vals[start:start + partition_size]) / l_p
+        parts.append((m_p, l_p, o_p))
+    big_m = max(m_p for m_p, _, _ in parts)
+    num = np.zeros(d, dtype=np.float64)
+    den = 0.0
+    for m_p, l_p, o_p in parts:
+        w = l_p * math.exp(m_p - big_m)
+        num += w * o_p
+        den += w
+    return num / den
