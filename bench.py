@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Paged decode benchmark on one MI355X.
+
+One step = the whole hot path over one batch: pa_cache_write of every
+sequence's new token, then pa_decode (partition kernel + log-sum-exp reduce).
+Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
+heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
+blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_167_amd", "csrc", "pa_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_partition_kernel_llama3_8b_traffic.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3_8b",
+                    choices=["llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
+                             "long_context_b16", "long_context_b32", "tiny_fp32"])
+    ap.add_argument("--partition", type=int, default=None,
+                    help="partition size in tokens (default: 256 for llama3_8b, 512 otherwise)")
+    ap.add_argument("--cold-iters", type=int, default=10,
+                    help="extra partition-kernel launches each after a 1 GiB cache flush")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def make_case(name):
+    import workloads as W
+    if name.startswith("long_context_b"):
+        return W.long_context(int(name.rsplit("b", 1)[1]))
+    return W.CONFIGS[name]()
+
+
+def kernel_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(config, partition):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken
+    on the current kernel source and the same workload; otherwise None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_sha() or t.get("config") != config or \
+            t.get("partition") != partition:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case):
+    """The oracle, as it stands, on the same workload: write the new tokens, then decode."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pa_oracle as O
+    log("cpu baseline: building the oracle's pools (not timed)")
+    kc, vc = O.cache_write(case.prefix_k, case.prefix_v, case.prefix_slots, case.empty_pool(),
+                           case.empty_pool(), case.block_size)
+    n = case.num_seqs
+    if case.kv_bytes() > 1.5e9:  # keep the CPU leg to tens of seconds: a prefix of the batch
+        n = max(1, int(n * 1.5e9 / case.kv_bytes()))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc, vc,
+                                 case.block_size)
+        O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n], case.scale,
+                 case.block_size, case.num_kv_heads)
+        dt = time.perf_counter() - t0
+    kv = int(case.context_lens[:n].astype("int64").sum()) * case.num_kv_heads * case.head_dim * \
+        2 * case.elt_bytes
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": dt, "seqs_per_s": n / dt,
+            "sample": f"{n} of {case.num_seqs} sequences, one step (write new tokens + decode), "
+                      "numpy float64, BLAS limited to 1 thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(decode shards by sequence or by kv head with no exchange between GPUs)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_167_amd as P
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    partition = args.partition
+    if partition is None:
+        partition = 256 if args.config == "llama3_8b" else 512
+
+    log(f"generating workload {args.config}")
+    t_gen = time.time()
+    case = make_case(args.config)
+    log(f"  {time.time() - t_gen:.1f} s; {case.num_seqs} seqs, kv bytes/step {case.kv_bytes()/1e9:.3f} GB")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q, tables, ctx = t(case.q), t(case.block_tables), t(case.context_lens)
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    tdt = torch.float16 if case.dtype == np.float16 else torch.float32
+    k_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+    v_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+    pk, pv, ps = t(case.prefix_k), t(case.prefix_v), t(case.prefix_slots)
+    P.pa_cache_write(pk, pv, ps, k_cache, v_cache)
+    del pk, pv, ps
+    new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
+    out = torch.empty_like(q)
+    mcl = case.max_context_len
+    ws_bytes = P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, mcl,
+                                           partition)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev0=None, ev1=None):
+        P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
+        if ev0 is not None:
+            ev0.record(stream)
+        P.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale,
+                               case.block_size, case.num_kv_heads, max_context_len=mcl,
+                               partition_size=partition, workspace=ws, stream=stream)
+        if ev1 is not None:
+            ev1.record(stream)
+        P.pa_decode_reduce(out, ctx, mcl, partition, ws, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        step(e0, e1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    kern_ms_avg = float(np.mean(kern_ms))
+
+    # cold-cache launches of the same kernel: a 1 GiB write evicts L2 and the 256 MB MALL
+    cold_ms = []
+    if args.cold_iters > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        for _ in range(args.cold_iters):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            step(e0, e1)
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del flush
+
+    kv_bytes = case.kv_bytes()
+    tokens_blocks = int(sum(-(-int(c) // case.block_size) for c in case.context_lens))
+    q_bytes = case.num_seqs * case.num_q_heads * case.head_dim * case.elt_bytes
+    alg_bytes = kv_bytes + q_bytes + tokens_blocks * 4 + case.num_seqs * 4
+    achieved = alg_bytes / (kern_ms_avg * 1e-3) / 1e9
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic = measured_traffic(args.config, partition)
+
+    result = {
+        "metric": "paged decode KV GB/s and % of MI355X HBM peak; sequences/s per layer",
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if case.dtype == np.float16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {"llama3_8b": "Llama-3-8B-shaped decode layer"}.get(args.config, args.config),
+            "num_seqs": case.num_seqs, "num_q_heads": case.num_q_heads,
+            "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
+            "block_size": case.block_size, "num_blocks": case.num_blocks,
+            "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}, "
+                            f"sum {int(case.context_lens.sum())}",
+            "partition_size": partition, "kv_bytes_per_step": kv_bytes,
+        },
+        "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
+        "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "roofline": {
+            "kernel": "pa_partition_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(kern_ms_avg * 1e3, 2),
+            "cold_avg_launch_us": round(float(np.mean(cold_ms)) * 1e3, 2) if cold_ms else None,
+            "cold_achieved": round(alg_bytes / (float(np.mean(cold_ms)) * 1e-3) / 1e9, 1)
+            if cold_ms else None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

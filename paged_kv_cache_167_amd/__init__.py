@@ -1,0 +1,18 @@
+"""Paged KV-cache decode attention for AMD MI355X.
+
+The computation lives in libpa.so (HIP kernels for gfx950, C ABI in
+include/pa.h); this package is its Python binding.
+"""
+from ._lib import (  # noqa: F401
+    DEFAULT_PARTITION,
+    PA_F16,
+    PA_F32,
+    PaError,
+    last_error,
+    lib,
+    pa_cache_write,
+    pa_decode,
+    pa_decode_partitions,
+    pa_decode_reduce,
+    pa_decode_workspace_bytes,
+)

@@ -265,6 +265,41 @@ def _tables_from(allocator: BlockAllocator, blocks_per_seq, width: int) -> np.nd
 # generic case
 # ---------------------------------------------------------------------------
 
+_LOGICAL_MEMO = {}  # one entry: the last logical data set (lets block-size sweeps reuse it)
+
+
+def _logical_data(lseed, ctx, num_q_heads, num_kv_heads, head_dim, sigma, dtype, variant):
+    """Queries and per-sequence logical K/V; a function of the logical seed only."""
+    if variant not in ("plain", "needle", "poscode"):
+        raise ValueError(f"unknown variant {variant!r}")
+    key = (lseed, tuple(int(c) for c in ctx), num_q_heads, num_kv_heads, head_dim, float(sigma),
+           np.dtype(dtype).str, variant)
+    if key in _LOGICAL_MEMO:
+        return _LOGICAL_MEMO[key]
+    _LOGICAL_MEMO.clear()
+    group = num_q_heads // num_kv_heads
+    q = _normal(np.random.default_rng([lseed, 0]), (len(ctx), num_q_heads, head_dim), sigma, dtype)
+    denom = float(max(int(max(ctx)) if len(ctx) else 1, 1))
+    needle_rng = np.random.default_rng([lseed, 9])
+    logical = []
+    for s, c in enumerate(ctx):
+        c = int(c)
+        rng = np.random.default_rng([lseed, 1, s])
+        k = _normal(rng, (c, num_kv_heads, head_dim), sigma, dtype)
+        v = _normal(rng, (c, num_kv_heads, head_dim), sigma, dtype)
+        if variant == "needle":
+            _plant_needle(k, q[s], int(needle_rng.integers(0, c)), group, dtype)
+        elif variant == "poscode":
+            _poscode(v, 0, denom, dtype)
+        logical.append((k, v))
+    _LOGICAL_MEMO[key] = (q, logical)
+    return q, logical
+
+
+def clear_memo() -> None:
+    _LOGICAL_MEMO.clear()
+
+
 def make_case(*, name="custom", seed=0, dtype=np.float16, context_lens, num_q_heads,
               num_kv_heads, head_dim, block_size, pool_factor=1.2, num_blocks=None,
               sigma=0.5, scale=None, variant="plain", extra_table_cols=0,
@@ -290,22 +325,12 @@ def make_case(*, name="custom", seed=0, dtype=np.float16, context_lens, num_q_he
     alloc = BlockAllocator(num_blocks, np.random.default_rng([seed, 7, block_size]))
     width = (max(blocks_per_seq) if blocks_per_seq else 1) + extra_table_cols
     tables = _tables_from(alloc, blocks_per_seq, width)
-    q = _normal(np.random.default_rng([lseed, 0]), (len(ctx), num_q_heads, head_dim), sigma, dtype)
-    denom = float(max(int(ctx.max()) if len(ctx) else 1, 1))
+    q, logical = _logical_data(lseed, ctx, num_q_heads, num_kv_heads, head_dim, sigma, dtype,
+                               variant)
     seq_tokens = []
-    needle_rng = np.random.default_rng([lseed, 9])
     for s, c in enumerate(ctx):
-        c = int(c)
-        rng = np.random.default_rng([lseed, 1, s])
-        k = _normal(rng, (c, num_kv_heads, head_dim), sigma, dtype)
-        v = _normal(rng, (c, num_kv_heads, head_dim), sigma, dtype)
-        if variant == "needle" and c > 0:
-            _plant_needle(k, q[s], int(needle_rng.integers(0, c)), group, dtype)
-        elif variant == "poscode" and c > 0:
-            _poscode(v, 0, denom, dtype)
-        elif variant != "plain" and variant not in ("needle", "poscode"):
-            raise ValueError(f"unknown variant {variant!r}")
-        slots = _slots(tables[s], np.arange(c), block_size)
+        k, v = logical[s]
+        slots = _slots(tables[s], np.arange(int(c)), block_size)
         seq_tokens.append((k, v, slots))
     meta = {"variant": variant, "seed": seed, "sigma": sigma}
     return _assemble(name, dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks,
