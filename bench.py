@@ -2,7 +2,8 @@
 """Paged decode benchmark on one MI355X.
 
 One step = the whole hot path over one batch: pa_cache_write of every
-sequence's new token, then pa_decode (partition kernel + log-sum-exp reduce).
+sequence's new token, then pa_decode (the stream kernel, whose persistent waves
+each take an equal share of the batch's tiles, then the log-sum-exp reduce).
 Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
 heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
 blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.
@@ -23,7 +24,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_167_amd", "csrc", "pa_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_partition_kernel_llama3_8b_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_stream_kernel_llama3_8b_traffic.json")
 
 
 def log(msg):
@@ -38,11 +39,15 @@ def parse():
     ap.add_argument("--config", default="llama3_8b",
                     choices=["llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
                              "long_context_b16", "long_context_b32", "tiny_fp32"])
-    ap.add_argument("--partition", type=int, default=None,
-                    help="partition size in tokens (default: 256 for llama3_8b, 512 otherwise)")
+    ap.add_argument("--partition", type=int, default=0,
+                    help="partition size in tokens (0: one wave per resident slot; >0: more "
+                         "waves, each taking at most about that many tokens)")
     ap.add_argument("--cold-iters", type=int, default=10,
-                    help="extra partition-kernel launches each after a 1 GiB cache flush")
+                    help="extra stream-kernel launches each after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a kernel of "
+                         "known traffic that scales the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -113,8 +118,6 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     partition = args.partition
-    if partition is None:
-        partition = 256 if args.config == "llama3_8b" else 512
 
     log(f"generating workload {args.config}")
     t_gen = time.time()
@@ -132,11 +135,17 @@ def main():
     new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
     out = torch.empty_like(q)
     mcl = case.max_context_len
-    ws_bytes = P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.head_dim, mcl,
-                                           partition)
+    ws_bytes = P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                           case.head_dim, mcl, partition)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    if args.calibrate_copy_mib > 0:
+        src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(ev0=None, ev1=None):
         P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
@@ -147,7 +156,7 @@ def main():
                                partition_size=partition, workspace=ws, stream=stream)
         if ev1 is not None:
             ev1.record(stream)
-        P.pa_decode_reduce(out, ctx, mcl, partition, ws, stream=stream)
+        P.pa_decode_reduce(out, ctx, case.num_kv_heads, mcl, partition, ws, stream=stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -182,7 +191,8 @@ def main():
     kv_bytes = case.kv_bytes()
     tokens_blocks = int(sum(-(-int(c) // case.block_size) for c in case.context_lens))
     q_bytes = case.num_seqs * case.num_q_heads * case.head_dim * case.elt_bytes
-    alg_bytes = kv_bytes + q_bytes + tokens_blocks * 4 + case.num_seqs * 4
+    # K/V rows, q in, out, the table entries in use and the context lengths
+    alg_bytes = kv_bytes + 2 * q_bytes + tokens_blocks * 4 + case.num_seqs * 4
     achieved = alg_bytes / (kern_ms_avg * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     traffic = measured_traffic(args.config, partition)
@@ -212,7 +222,7 @@ def main():
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "roofline": {
-            "kernel": "pa_partition_kernel",
+            "kernel": "pa_stream_kernel",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

@@ -78,13 +78,14 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
 /*
  * pa_decode_workspace_bytes -- workspace pa_decode needs for these sizes.
  *
- * With partition_size > 0 a sequence of ctx tokens is split into
- * ceil(ctx / partition_size) partitions; each partition's maximum, exp-sum and
- * normalised output (fp32) are kept here until the reduce merges them.
- * Returns 0 when partition_size == 0 (single pass) or any size is <= 0.
+ * The workspace holds, per (sequence, kv head, tile of query heads), which of the
+ * decode's persistent waves hold pieces of that context, and per wave up to two
+ * piece records (fp32 running max, exp-sum and normalised output of each query
+ * head).  Its size depends only on the arguments below, never on the device.
+ * Returns 0 for num_seqs <= 0 or invalid sizes.
  */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_decode -- single-query attention of every (sequence, query head) over the
@@ -99,24 +100,28 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * The result equals attention over contiguously stored K/V ([SOSP] sections 3.3
  * and 4.4).  A context of 0 gives a zero row.
  *
- * partition_size > 0 (a multiple of block_size) splits each context into
- * partitions of that many tokens that run as separate work-groups; a second kernel
- * merges them by log-sum-exp in partition order.  partition_size == 0 runs one
- * pass per sequence and needs no workspace.  Results depend only on logical
- * positions, so they are bitwise identical under any relabelling of physical blocks.
+ * Work split: the batch is cut into tiles of consecutive tokens and persistent
+ * waves each take an equal run of them, so a long context is split over several
+ * waves; a second kernel merges the pieces of each context by log-sum-exp, in
+ * token order.  partition_size == 0 uses as many waves as the GPU holds at once;
+ * partition_size > 0 (a multiple of block_size) adds waves until each takes about
+ * that many tokens at most.  Results are bitwise identical under any relabelling of
+ * physical blocks and any block size; where a context is split depends on the whole
+ * batch, so the same sequence at another batch position may differ in rounding.
  *
  * out                device, [num_seqs, num_q_heads, head_dim], dtype; written
  * q                  device, [num_seqs, num_q_heads, head_dim], dtype
  * k_cache, v_cache   device, [num_blocks, num_kv_heads, block_size, head_dim], dtype
  * block_tables       device, [num_seqs, max_blocks_per_seq] int32
  * context_lens       device, [num_seqs] int32
- * max_context_len    host bound on every context_lens[s]; sizes the grid
- * workspace          device, >= pa_decode_workspace_bytes(...) bytes (may be NULL if 0)
+ * max_context_len    host bound on every context_lens[s]; at most max_blocks_per_seq * block_size
+ * workspace          device, >= pa_decode_workspace_bytes(...) bytes, 256-byte aligned;
+ *                    contents need no initialisation and are scratch between calls
  *
  * Device-side checks: a sequence whose context length is negative or exceeds
- * max_context_len or max_blocks_per_seq * block_size, or whose table names a block
- * outside [0, num_blocks) within its context, reads nothing invalid and gets NaN
- * in every output element of the affected query heads.
+ * max_context_len gets NaN rows and reads nothing; a table entry outside
+ * [0, num_blocks) within a context is not dereferenced (block 0 is read instead) and
+ * the affected query heads get NaN.  Calls that share a workspace must not overlap.
  * returns PA_OK, or a negative code with nothing launched.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -129,12 +134,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 
 /*
  * pa_decode_partitions / pa_decode_reduce -- the two launches pa_decode makes,
- * callable on their own (for timing each kernel, or to merge partitions computed
- * elsewhere).  pa_decode_partitions takes pa_decode's arguments; sequences with a
- * single partition are written to out directly, the others leave their partition
- * results in the workspace.  pa_decode_reduce merges those into out; it must see
- * the same context_lens, sizes and workspace.  pa_decode_reduce with
- * partition_size == 0 does nothing.
+ * callable on their own (to time each kernel, or to merge pieces computed
+ * elsewhere).  pa_decode_partitions takes pa_decode's arguments; it writes the rows
+ * of contexts held whole by one wave and leaves the pieces of split contexts in the
+ * workspace.  pa_decode_reduce writes every other row (merged pieces, zero rows for
+ * empty contexts, NaN rows for invalid ones); it must see the same context_lens,
+ * sizes and workspace, and run after pa_decode_partitions on the same stream.
  */
 int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* context_lens,
@@ -145,7 +150,7 @@ int pa_decode_partitions(void* out, const void* q, const void* k_cache, const vo
                          void* workspace, size_t workspace_bytes, void* stream);
 
 int pa_decode_reduce(void* out, const int32_t* context_lens,
-                     int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t max_context_len, int32_t partition_size, int32_t dtype,
                      const void* workspace, size_t workspace_bytes, void* stream);
 
@@ -154,7 +159,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((1 << 16) | 0)
+#define PA_ABI_VERSION ((2 << 16) | 0)
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
 
-DEFAULT_PARTITION = 512
+DEFAULT_PARTITION = 0  # 0: as many persistent waves as the GPU holds
 
 _c_int32 = ctypes.c_int32
 _c_int64 = ctypes.c_int64
@@ -33,7 +33,8 @@ _vp = ctypes.c_void_p
 SIGNATURES = {
     "pa_cache_write": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32,
                                   _c_int64, _c_int32, _vp]),
-    "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                                    _c_int32]),
     "pa_decode": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_int32,
                              _c_int32, _vp, ctypes.c_size_t, _vp]),
@@ -41,7 +42,7 @@ SIGNATURES = {
                                         _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                         _c_int64, _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_reduce": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
-                                    _c_int32, _vp, ctypes.c_size_t, _vp]),
+                                    _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_c_int32, []),
 }
@@ -112,10 +113,10 @@ def pa_cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     _check("pa_cache_write", code)
 
 
-def pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                               partition_size=DEFAULT_PARTITION) -> int:
-    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                               partition_size))
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, partition_size))
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
@@ -126,8 +127,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, bl
     max_blocks = block_tables.shape[1]
     if max_context_len is None:  # the table width bounds every context without a device sync
         max_context_len = max_blocks * block_size
-    need = pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
-                                     partition_size)
+    need = pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                     max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -155,7 +156,7 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                          num_kv_heads, max_context_len=None, partition_size=DEFAULT_PARTITION,
                          workspace=None, stream=None):
-    """First launch of pa_decode; returns the workspace holding the partition results."""
+    """First launch of pa_decode; returns the workspace holding the pieces of split contexts."""
     args, workspace = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                                    block_size, num_kv_heads, max_context_len, partition_size,
                                    workspace, stream)
@@ -163,12 +164,14 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, s
     return workspace
 
 
-def pa_decode_reduce(out, context_lens, max_context_len, partition_size, workspace, stream=None):
-    """Second launch of pa_decode: merge the partitions left in the workspace into out."""
+def pa_decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition_size, workspace,
+                     stream=None):
+    """Second launch of pa_decode: merge the pieces left in the workspace into out."""
     num_seqs, num_q_heads, head_dim = out.shape
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    code = lib().pa_decode_reduce(_ptr(out), _ptr(context_lens), num_seqs, num_q_heads, head_dim,
-                                  int(max_context_len), int(partition_size), _dtype_code(out),
-                                  ws_ptr, ws_bytes, _stream(out, stream))
+    code = lib().pa_decode_reduce(_ptr(out), _ptr(context_lens), num_seqs, num_q_heads,
+                                  int(num_kv_heads), head_dim, int(max_context_len),
+                                  int(partition_size), _dtype_code(out), ws_ptr, ws_bytes,
+                                  _stream(out, stream))
     _check("pa_decode_reduce", code)

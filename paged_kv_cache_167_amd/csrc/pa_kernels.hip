@@ -2,9 +2,9 @@
 //
 // Three kernels:
 //   pa_cache_write_kernel  -- scatter each new token's K/V row into its slot.
-//   pa_partition_kernel    -- attention of one (sequence, kv head, query-head tile,
-//                             context partition) over the paged K/V.
-//   pa_reduce_kernel       -- log-sum-exp merge of a sequence's partitions.
+//   pa_stream_kernel       -- attention over the paged K/V, the whole batch streamed
+//                             by persistent waves that each own an equal share of it.
+//   pa_reduce_kernel       -- log-sum-exp merge of the pieces a context was split into.
 //
 // Sources (page title, section):
 //  [DRV]  "揭开 NVIDIA 驱动栈的面纱：GPU 显存页表与 vLLM 中的 PagedAttention 是如何在底层协同的"
@@ -13,33 +13,40 @@
 //  [SRC]  vLLM source walk-through (peacm.com), section 3.2 (append into the last
 //         block), section 3.4 (loop over logical blocks, tail mask, online softmax).
 //  [CON]  "PagedAttention：当 KV Cache 遇到操作系统分页" (forceinjection.github.io),
-//         section 3.2 (the kernel walks the table block by block); section 5.1 (keep
-//         the table slice in fast memory to hide the software translation).
+//         section 3.2 (the kernel walks the table block by block); section 5.1 (the
+//         software translation costs kernel time; keep the table lookups cheap).
 //  [SOSP] "《Efficient Memory Management for LLM Serving with PagedAttention》深度解读报告"
 //         (zako-mio.github.io), sections 2.3 and 3.3 (only the filled slots of a block
 //         take part; the result equals attention over contiguous K/V).
 //
 // Design for gfx950 (not a translation of the pages' CUDA kernel):
 //  * The pool layout [N, Hkv, B, D] makes one (block, kv head) tile a contiguous
-//    B*D run, so a wave reads it with 16-byte loads whose lanes cover whole rows.
-//  * All G query heads that share a kv head are handled by one work-group, so each
-//    K/V tile is read from HBM once per group (GQA), not once per query head.
-//  * K pass: C lanes share one token row; each multiplies its 16-byte chunks with
-//    the matching q chunks (v_dot2 for fp16), and the C partial sums are combined
-//    with DPP row permutations fused into the adds.  Scores go to LDS.
-//  * Softmax: one wave per query row takes the chunk max and exp-sum with wave
-//    shuffles; the running max and sum carry over chunks (online softmax, [SRC] 3.4).
-//  * V pass: a whole 16-byte chunk per lane (CV lanes per row), fp32 accumulators.
-//  * Contexts are split into partitions (split-K) so that short batches still fill
-//    256 CUs; a second kernel merges them in partition order.
-//  * Every reduction runs in a fixed order that depends only on logical positions,
-//    so results are bitwise reproducible under any physical block placement.
+//    B*D run; a wave reads 16 token rows at a time with 16-byte loads.
+//  * All G query heads that share a kv head are handled by one wave, so each K/V
+//    row is read from HBM once per group (GQA), not once per query head.
+//  * Work split ("stream-K"): the batch is flattened into tiles of consecutive tokens
+//    ordered by (sequence, kv head, position) and every persistent wave takes an
+//    equal, contiguous run of tiles.  A context split between waves leaves one
+//    partial result per piece; the reduce kernel merges the pieces by log-sum-exp.
+//    Load balance is exact whatever the mix of context lengths.
+//  * Each wave keeps a two-stage ring in LDS filled by direct global->LDS loads, so
+//    two tiles are in flight during arithmetic without holding them in registers.
+//    Block-table entries and context lengths are wave-uniform and come in through
+//    scalar loads, which never wait behind the vector loads.
+//  * C lanes share a token row for both K and V.  Scores: v_dot2 products of the
+//    lane's 16-byte chunks with the matching q chunks, summed over the C lanes with
+//    DPP row permutations fused into the adds; the probability is applied to the V
+//    chunks the same lanes hold.  Each token group keeps its own online-softmax
+//    state (running max and sum, [SRC] 3.4); the groups merge at the end of a piece.
+//  * Results depend only on logical positions and the fixed work split, so they are
+//    bitwise reproducible under any physical block placement or block size.
 
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "pa.h"
@@ -51,10 +58,7 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;                 // waves per decode work-group
-constexpr int kThreads = kWaves * kWave;  // 256
-constexpr int kChunk = 512;               // tokens whose scores are held in LDS at once
-constexpr int kMinBlock = 8;              // smallest supported block size
+constexpr int kMaxWaves = 4096;  // persistent waves in the default split (MI355X holds 2048+)
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -66,6 +70,9 @@ __device__ __forceinline__ float dpp_f(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 
+__device__ __forceinline__ float as_f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned as_u(float f) { return __builtin_bit_cast(unsigned, f); }
+
 // Sum over aligned groups of C consecutive lanes (C <= 16); every lane of the group
 // ends with the same value.  Steps: swap neighbours, swap pairs (quad_perm), then
 // mirror within 8 and within 16 lanes, which pair each lane with one in the other half.
@@ -76,6 +83,19 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (C >= 4) x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]
   if constexpr (C >= 8) x += dpp_f<0x141>(x);  // row_half_mirror
   if constexpr (C >= 16) x += dpp_f<0x140>(x); // row_mirror
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int x, int lane) {
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
   return x;
 }
 
@@ -120,35 +140,101 @@ __device__ __forceinline__ float dot16<float>(const u32x4& a, const u32x4& b, fl
   return acc;
 }
 
+// acc[j*E + e] += p * v[j][e] over the lane's chunks of one V row (fp16 halves go
+// straight into v_fma_mix_f32).
 template <typename T>
-__device__ __forceinline__ void unpack16(const u32x4& v, float* f);
+struct PV;
 
 template <>
-__device__ __forceinline__ void unpack16<f16>(const u32x4& v, float* f) {
+struct PV<f16> {
+  template <int NL>
+  __device__ __forceinline__ static void run(float* acc, float p, const u32x4 (&v)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f16x2 h = word_as<f16x2>(v[j], i);
+        acc[j * 8 + 2 * i] = fmaf(p, static_cast<float>(h.x), acc[j * 8 + 2 * i]);
+        acc[j * 8 + 2 * i + 1] = fmaf(p, static_cast<float>(h.y), acc[j * 8 + 2 * i + 1]);
+      }
+  }
+};
+
+template <>
+struct PV<float> {
+  template <int NL>
+  __device__ __forceinline__ static void run(float* acc, float p, const u32x4 (&v)[NL]) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j * 4 + i] = fmaf(p, word_as<float>(v[j], i), acc[j * 4 + i]);
+  }
+};
+
+// Pack E fp32 values into one 16-byte chunk of T (round to nearest even for fp16).
+template <typename T>
+__device__ __forceinline__ u32x4 pack16(const float* x);
+
+template <>
+__device__ __forceinline__ u32x4 pack16<f16>(const float* x) {
+  u32x4 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16x2 h = word_as<f16x2>(v, i);
-    f[2 * i] = static_cast<float>(h.x);
-    f[2 * i + 1] = static_cast<float>(h.y);
+    const f16x2 h = {static_cast<f16>(x[2 * i]), static_cast<f16>(x[2 * i + 1])};
+    r[i] = __builtin_bit_cast(uint32_t, h);
   }
+  return r;
 }
 
 template <>
-__device__ __forceinline__ void unpack16<float>(const u32x4& v, float* f) {
+__device__ __forceinline__ u32x4 pack16<float>(const float* x) {
+  u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = word_as<float>(v, i);
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, x[i]);
+  return r;
 }
 
-// Lanes per token row in the K pass: enough that the q chunks a lane keeps in
-// registers stay near 32 VGPRs (64 for 8-row tiles), never fewer than a quarter
-// of a row's 16-byte chunks, never more than all of them.
-constexpr int pick_k_lanes(int row_bytes, int gt) {
-  int cv = row_bytes / 16;
-  int c = row_bytes * gt / 128;
-  if (gt >= 8) c /= 2;
-  if (c < cv / 4) c = cv / 4;
+// 2^(a - b) that is 0 when a is -inf (an empty running state), never NaN.
+__device__ __forceinline__ float rescale(float a, float b) {
+  return a == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a - b);
+}
+
+// Read one ring stage back: wait until at most VMCNT vector-memory operations are
+// outstanding (the stage's own direct-to-LDS loads are older than those, and loads
+// complete in order), then read the lane's eight 16-byte words at base + 16*lane +
+// 1024*i, then wait for the reads.  Written as one asm block so that the compiler's
+// conservative tracking of direct-to-LDS loads cannot add a full drain in front of the
+// reads; the memory clobber keeps every other memory access on its side of the block.
+template <int VMCNT>
+__device__ __forceinline__ void read_stage8(uint32_t lds_addr, u32x4 (&o)[8]) {
+  asm volatile(
+      "s_waitcnt vmcnt(%9)\n\t"
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %8 offset:1024\n\t"
+      "ds_read_b128 %2, %8 offset:2048\n\t"
+      "ds_read_b128 %3, %8 offset:3072\n\t"
+      "ds_read_b128 %4, %8 offset:4096\n\t"
+      "ds_read_b128 %5, %8 offset:5120\n\t"
+      "ds_read_b128 %6, %8 offset:6144\n\t"
+      "ds_read_b128 %7, %8 offset:7168\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(o[0]), "=v"(o[1]), "=v"(o[2]), "=v"(o[3]), "=v"(o[4]), "=v"(o[5]), "=v"(o[6]),
+        "=v"(o[7])
+      : "v"(lds_addr), "n"(VMCNT)
+      : "memory");
+}
+
+// Lanes that share one token row.  Each lane keeps its q chunks in registers, so the
+// row is split finely enough that they stay near 32 VGPRs.  At least 8 lanes per row:
+// a row slot then spans at most 64/8 = 8 consecutive tokens, which never straddle a
+// block (B >= 8), so its block-table entry is one wave-uniform scalar load.  At most
+// 16 lanes (one DPP row) and at most the row's number of 16-byte chunks.
+constexpr int pick_row_lanes(int row_bytes, int gt) {
+  const int cv = row_bytes / 16;
+  int c = gt * row_bytes / 128;
+  if (c < 8) c = 8;
+  if (c > 16) c = 16;
   if (c > cv) c = cv;
-  if (c < 1) c = 1;
   return c;
 }
 
@@ -156,16 +242,17 @@ template <typename T, int D, int GT>
 struct Cfg {
   static constexpr int kRow = D * static_cast<int>(sizeof(T));  // bytes per token row
   static constexpr int kE = 16 / static_cast<int>(sizeof(T));   // elements per 16-byte chunk
-  static constexpr int kCV = kRow / 16;                         // lanes per row, V pass
-  static constexpr int kC = pick_k_lanes(kRow, GT);             // lanes per row, K pass
-  static constexpr int kNLK = kRow / (16 * kC);                 // chunks per lane per row, K pass
-  static constexpr int kRK = kNLK >= 8 ? 1 : 8 / kNLK;          // rows per lane per K step
-  static constexpr int kTK = kRK * (kWave / kC);                // tokens per wave per K step
-  static constexpr int kRV = 8;                                 // rows per lane per V step
-  static constexpr int kTV = kRV * (kWave / kCV);               // tokens per wave per V step
-  static constexpr int kLds = (kChunk * GT > kWaves * GT * D) ? kChunk * GT : kWaves * GT * D;
-  static_assert(kChunk % kTK == 0 && kChunk % kTV == 0, "chunk must hold whole steps");
-  static_assert(kC <= 16, "K-pass group wider than one DPP row");
+  static constexpr int kCV = kRow / 16;                         // 16-byte chunks per row
+  static constexpr int kC = pick_row_lanes(kRow, GT);           // lanes per token row
+  static constexpr int kNL = kCV / kC;                          // chunks per lane per row
+  static constexpr int kDL = kNL * kE;                          // elements per lane per row
+  static constexpr int kGroups = kWave / kC;                    // token groups in a wave
+  static constexpr int kRK = 4 / kNL;                           // rows per lane per tile
+  static constexpr int kTK = kRK * kGroups;                     // tokens per tile
+  static constexpr int kSlots = kRK * kNL * 2;                  // 1 KB LDS slots per tile
+  static_assert(kC * kNL == kCV && kNL <= 4, "row split");
+  static_assert(kSlots == 8, "a tile is eight 1 KB slots (read_stage8)");
+  static_assert(kGroups <= 8, "a row slot must lie in one block of at least 8 tokens");
 };
 
 // ---------------------------------------------------------------------------
@@ -196,14 +283,17 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// decode, pass 1: one work-group per (partition, kv head x q-head tile, sequence)
+// decode, pass 1: persistent waves streaming equal shares of the batch
 // ---------------------------------------------------------------------------
 
-struct PartitionArgs {
+// A segment is one (sequence, unit) pair, unit = (kv head, tile of GT query heads);
+// it has ceil(ctx / TK) tiles.  Segments are ordered by sequence, then unit.
+struct StreamArgs {
   void* out;
-  float* ws_m;  // [S, Hq, max_parts]  running max of each partition (log2 units)
-  float* ws_l;  // [S, Hq, max_parts]  exp-sum of each partition
-  float* ws_o;  // [S, Hq, max_parts, D] normalised output of each partition
+  int2* seg_desc;  // [S * n_units] {first wave, last wave} holding pieces of the segment
+  float* rec_m;    // [2 * W * GT] per piece record: running max (log2 units) per row
+  float* rec_l;    // [2 * W * GT] exp-sum per row
+  float* rec_o;    // [2 * W * GT * D] normalised output per row
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -214,246 +304,403 @@ struct PartitionArgs {
   int log2_block;
   int num_kv_heads;
   int num_q_heads;
-  int group;       // query heads per kv head
-  int n_gtiles;    // ceil(group / GT)
+  int group;     // query heads per kv head
+  int n_gtiles;  // ceil(group / GT)
+  int n_units;   // num_kv_heads * n_gtiles
+  int num_seqs;
   int max_blocks_per_seq;
   int max_context_len;
   int64_t num_blocks;
-  int partition_size;
-  int max_parts;
+  int num_waves;
+};
+
+// Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
+struct Cursor {
+  int s;       // sequence
+  int unit;    // kv head * n_gtiles + query-head tile
+  int t;       // tile within the segment
+  int nt;      // tiles in the segment
+  int ctx;     // context length of the sequence
+  int gstart;  // global index of the segment's first tile
 };
 
 template <typename T, int D, int GT>
-__global__ __launch_bounds__(kThreads) void pa_partition_kernel(const PartitionArgs a) {
+__global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   using K = Cfg<T, D, GT>;
-  __shared__ float s_buf[K::kLds];              // scores, then probabilities, then partial sums
-  __shared__ int s_tbl[kChunk / kMinBlock];     // physical ids of the chunk's blocks (-1 = invalid)
-  __shared__ float s_m[GT], s_l[GT], s_corr[GT];
-  __shared__ int s_bad;
+  constexpr int RK = K::kRK, NL = K::kNL, DL = K::kDL, C = K::kC, E = K::kE, TK = K::kTK;
+  constexpr int GR = K::kGroups;
+  __shared__ __align__(16) u32x4 s_stage0[8][kWave];
+  __shared__ __align__(16) u32x4 s_stage1[8][kWave];
 
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y / a.n_gtiles;
-  const int gtile = blockIdx.y - kvh * a.n_gtiles;
-  const int s = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid / kWave;
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int sub = lane % C;  // which chunks of a row this lane holds
+  const int grp = lane / C;  // which token of a row slot this lane holds
+  const int S = a.num_seqs;
+  const int32_t* ctxs = a.context_lens;
+  auto seg_tiles = [&](int ctx) {  // invalid or empty contexts contribute no tiles
+    return (ctx > 0 && ctx <= a.max_context_len) ? (ctx + TK - 1) / TK : 0;
+  };
 
-  const int ctx = a.context_lens[s];
-  const bool bad_ctx = ctx < 0 || ctx > a.max_context_len;
-  const int nparts = (bad_ctx || ctx == 0) ? 1 : (ctx + a.partition_size - 1) / a.partition_size;
-  if (part >= nparts) return;
+  // ---- total tiles and this wave's share [A, A + n_my)
+  int part = 0;
+  for (int b = 0; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
+  const int total = wave_sum_int(part) * a.n_units;
+  const int W = a.num_waves;
+  const int Q = total / W, R = total - (total / W) * W;
+  const int A = w * Q + min(w, R);
+  const int n_my = Q + (w < R ? 1 : 0);
+  if (n_my == 0) return;
+  const int A_end = A + n_my;
+  auto wave_of = [&](int x) {  // owner of global tile x
+    const int cut = R * (Q + 1);
+    return x < cut ? x / (Q + 1) : R + (x - cut) / Q;
+  };
 
-  const int h0 = kvh * a.group + gtile * GT;
-  const int ng = min(GT, a.group - gtile * GT);  // real rows in this tile
-  const int64_t row0 = static_cast<int64_t>(s) * a.num_q_heads + h0;
-  T* out = static_cast<T*>(a.out);
-
-  if (bad_ctx || ctx == 0) {  // nothing to attend over: zeros, or NaN for an invalid length
-    const T fill = static_cast<T>(bad_ctx ? __builtin_nanf("") : 0.0f);
-    for (int i = tid; i < ng * D; i += kThreads) out[row0 * D + i] = fill;
-    return;
+  // ---- locate tile A: the sequence whose tiles cover it
+  int s0 = 0, base = 0;  // base: global index of s0's first tile
+  for (int b = 0; b < S; b += kWave) {
+    const int ts = ((b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0) * a.n_units;
+    const int incl = wave_incl_scan_int(ts, lane);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > A);
+    if (hit != 0) {
+      const int l = __builtin_ctzll(hit);
+      s0 = b + l;
+      base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
+      break;
+    }
+    base += __builtin_amdgcn_readlane(incl, kWave - 1);
   }
+  Cursor cc;  // the tile being computed
+  cc.s = s0;
+  cc.ctx = ctxs[s0];
+  cc.nt = seg_tiles(cc.ctx);
+  cc.unit = (A - base) / cc.nt;
+  cc.t = (A - base) - cc.unit * cc.nt;
+  cc.gstart = base + cc.unit * cc.nt;
+  auto advance = [&](Cursor& c) {
+    if (++c.t < c.nt) return;
+    c.gstart += c.nt;
+    c.t = 0;
+    if (++c.unit < a.n_units) return;
+    c.unit = 0;
+    do {
+      ++c.s;
+      c.ctx = c.s < S ? ctxs[c.s] : 0;
+      c.nt = seg_tiles(c.ctx);
+    } while (c.nt == 0 && c.s < S);
+  };
 
-  const int t_begin = part * a.partition_size;
-  const int t_end = min(ctx, t_begin + a.partition_size);
-
-  // q chunks for the K pass: lane sub holds row chunks j*C + sub (j < NLK).
-  const int subk = lane % K::kC;
-  const T* qp = static_cast<const T*>(a.q);
-  u32x4 qk[GT][K::kNLK];
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int j = 0; j < K::kNLK; ++j)
-      qk[g][j] = (g < ng) ? load16(qp + (row0 + g) * D + (j * K::kC + subk) * K::kE)
-                          : u32x4{0u, 0u, 0u, 0u};
-
-  if (tid == 0) s_bad = 0;
-  if (tid < GT) {
-    s_m[tid] = -INFINITY;
-    s_l[tid] = 0.0f;
-  }
-
-  float acc[GT][K::kE];
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < K::kE; ++e) acc[g][e] = 0.0f;
-
-  const int32_t* tbl_row = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
-  const int64_t head_stride = static_cast<int64_t>(a.block_size) * D;  // elements
-  const int64_t block_stride = head_stride * a.num_kv_heads;
-  const T* kbase = static_cast<const T*>(a.k_cache) + kvh * head_stride;
-  const T* vbase = static_cast<const T*>(a.v_cache) + kvh * head_stride;
+  // ---- direct-to-LDS loads of one tile into a ring stage
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+  const uint32_t head_bytes = static_cast<uint32_t>(a.block_size * D * sizeof(T));
+  const uint32_t block_bytes = head_bytes * static_cast<uint32_t>(a.num_kv_heads);
   const int bmask = a.block_size - 1;
-  const int subv = lane % K::kCV;
-
-  for (int c0 = t_begin; c0 < t_end; c0 += kChunk) {
-    const int n = min(kChunk, t_end - c0);
-    const int b0 = c0 >> a.log2_block;  // c0 is a multiple of the block size
-    const int nb = (n + bmask) >> a.log2_block;
-    __syncthreads();  // the previous chunk is done with s_tbl and s_buf
-    for (int i = tid; i < nb; i += kThreads) {
-      const int phys = tbl_row[b0 + i];
-      s_tbl[i] = (phys < 0 || phys >= a.num_blocks) ? -1 : phys;
-    }
-    __syncthreads();
-
-    // ---- K pass: scores of every query row for every token of the chunk
-    for (int tile = w; tile * K::kTK < n; tile += kWaves) {
-      u32x4 kr[K::kRK][K::kNLK];
+  // Issue the loads of tile f (a phantom tile past the wave's share reads rows of
+  // block 0, kv head 0: a valid address whose data is never used).  Returns whether a
+  // table entry of the tile lies outside the pool (then block 0 is read instead).
+  auto fetch = [&](const Cursor& f, bool real, int st) -> bool {
+    bool bad = false;
+    const int kvh = real ? f.unit / a.n_gtiles : 0;
+    const int32_t* trow = a.block_tables + static_cast<int64_t>(real ? f.s : 0) * a.max_blocks_per_seq;
 #pragma unroll
-      for (int r = 0; r < K::kRK; ++r) {
-        const int tok = tile * K::kTK + r * (kWave / K::kC) + lane / K::kC;
-        int phys = (tok < n) ? s_tbl[tok >> a.log2_block] : 0;
-        if (phys < 0) {  // invalid table entry inside the context: poison, read block 0
-          s_bad = 1;
-          phys = 0;
-        }
-        const T* p = kbase + phys * block_stride + static_cast<int64_t>(tok & bmask) * D;
-#pragma unroll
-        for (int j = 0; j < K::kNLK; ++j) kr[r][j] = load16(p + (j * K::kC + subk) * K::kE);
-      }
-#pragma unroll
-      for (int r = 0; r < K::kRK; ++r) {
-        const int tok = tile * K::kTK + r * (kWave / K::kC) + lane / K::kC;
-#pragma unroll
-        for (int g = 0; g < GT; ++g) {
-          float d = 0.0f;
-#pragma unroll
-          for (int j = 0; j < K::kNLK; ++j) d = dot16<T>(qk[g][j], kr[r][j], d);
-          d = group_sum<K::kC>(d);
-          if (tok < n && (g % K::kC) == subk) s_buf[tok * GT + g] = d * a.scale_log2;
+    for (int r = 0; r < RK; ++r) {
+      const int tok0 = f.t * TK + r * GR;  // first token of the row slot (wave-uniform)
+      int p = 0;
+      if (real && tok0 < f.ctx) {
+        p = trow[tok0 >> a.log2_block];  // scalar load
+        if (p < 0 || p >= a.num_blocks) {
+          bad = true;
+          p = 0;
         }
       }
+      const uint32_t row = static_cast<uint32_t>(((tok0 + grp) & bmask) * D * sizeof(T)) +
+                           static_cast<uint32_t>(sub * 16);
+      const uint64_t off = static_cast<uint64_t>(static_cast<uint32_t>(p)) * block_bytes +
+                           static_cast<uint64_t>(kvh) * head_bytes + row;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        u32x4* slot = st == 0 ? &s_stage0[(r * NL + j) * 2][0] : &s_stage1[(r * NL + j) * 2][0];
+        __builtin_amdgcn_global_load_lds(kcache + off + j * C * 16, slot, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vcache + off + j * C * 16, slot + kWave, 16, 0, 0);
+      }
     }
-    __syncthreads();
+    return bad;
+  };
+  const uint32_t stage_lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_stage0[0][lane]));
+  const uint32_t stage_lds1 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&s_stage1[0][lane]));
+  // Read a stage back (each lane reads the 16-byte words it loaded).  At least 8 loads
+  // are issued after a stage's own loads before it is read, so waiting until at most 8
+  // are outstanding never waits for less than that stage.
+  auto unstage = [&](int st, u32x4 (&kb)[RK][NL], u32x4 (&vb)[RK][NL]) {
+    u32x4 o[8];
+    read_stage8<8>(st == 0 ? stage_lds0 : stage_lds1, o);
+#pragma unroll
+    for (int r = 0; r < RK; ++r)
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        kb[r][j] = o[(r * NL + j) * 2];
+        vb[r][j] = o[(r * NL + j) * 2 + 1];
+      }
+  };
 
-    // ---- softmax over the chunk: one wave per query row
-    for (int g = w; g < GT; g += kWaves) {
-      float mx = -INFINITY;
-      for (int t = lane; t < n; t += kWave) mx = fmaxf(mx, s_buf[t * GT + g]);
-      mx = wave_max(mx);
-      const float m_old = s_m[g];
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.0f;
-      for (int t = lane; t < n; t += kWave) {
-        const float e = __builtin_amdgcn_exp2f(s_buf[t * GT + g] - m_new);
-        s_buf[t * GT + g] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        const float corr = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 on the first chunk
-        s_corr[g] = corr;
-        s_l[g] = s_l[g] * corr + sum;
-        s_m[g] = m_new;
-      }
-    }
-    __syncthreads();
+  // ---- per-piece state: q rows, and per token group the running max, sum, output
+  u32x4 qv[GT][NL];
+  float m[GT], l[GT], acc[GT][DL];
+  int h0 = 0, ng = 0;
+  bool piece_bad = false;
+  const T* qp = static_cast<const T*>(a.q);
 
-    // ---- V pass: acc = acc * corr + sum_t p_t v_t
-#pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      const float corr = s_corr[g];
-#pragma unroll
-      for (int e = 0; e < K::kE; ++e) acc[g][e] *= corr;
-    }
-    for (int tile = w; tile * K::kTV < n; tile += kWaves) {
-      u32x4 vr[K::kRV];
-#pragma unroll
-      for (int r = 0; r < K::kRV; ++r) {
-        const int tok = tile * K::kTV + r * (kWave / K::kCV) + lane / K::kCV;
-        int phys = (tok < n) ? s_tbl[tok >> a.log2_block] : 0;
-        phys = phys < 0 ? 0 : phys;  // already flagged in the K pass
-        vr[r] = load16(vbase + phys * block_stride + static_cast<int64_t>(tok & bmask) * D +
-                       subv * K::kE);
-      }
-#pragma unroll
-      for (int r = 0; r < K::kRV; ++r) {
-        const int tok = tile * K::kTV + r * (kWave / K::kCV) + lane / K::kCV;
-        if (tok < n) {  // rows past the chunk were read from block 0 and are never used
-          float vf[K::kE];
-          unpack16<T>(vr[r], vf);
-#pragma unroll
-          for (int g = 0; g < GT; ++g) {
-            const float p = s_buf[tok * GT + g];
-#pragma unroll
-            for (int e = 0; e < K::kE; ++e) acc[g][e] = fmaf(p, vf[e], acc[g][e]);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- combine: across the wave's token groups, then across waves in wave order
-#pragma unroll
-  for (int g = 0; g < GT; ++g)
-#pragma unroll
-    for (int e = 0; e < K::kE; ++e)
-      for (int o = K::kCV; o < kWave; o <<= 1) acc[g][e] += __shfl_xor(acc[g][e], o);
-  __syncthreads();  // probabilities are no longer needed
-  if (lane < K::kCV) {
+  auto piece_start = [&]() {
+    const int kvh = cc.unit / a.n_gtiles;
+    const int gtile = cc.unit - kvh * a.n_gtiles;
+    h0 = kvh * a.group + gtile * GT;
+    ng = min(GT, a.group - gtile * GT);
+    const int64_t row0 = static_cast<int64_t>(cc.s) * a.num_q_heads + h0;
 #pragma unroll
     for (int g = 0; g < GT; ++g)
 #pragma unroll
-      for (int e = 0; e < K::kE; ++e) s_buf[(w * GT + g) * D + lane * K::kE + e] = acc[g][e];
-  }
-  __syncthreads();
-
-  const bool bad = s_bad != 0;
-  const float qnan = __builtin_nanf("");
-  for (int i = tid; i < ng * D; i += kThreads) {
-    const int g = i / D;
-    const int d = i - g * D;
-    float sum = 0.0f;
+      for (int j = 0; j < NL; ++j)
+        qv[g][j] = (g < ng) ? load16(qp + (row0 + g) * D + (j * C + sub) * E) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) sum += s_buf[(ww * GT + g) * D + d];
-    const float l = s_l[g];
-    const float o = bad ? qnan : sum / l;
-    if (nparts == 1) {
-      out[(row0 + g) * D + d] = static_cast<T>(o);
-    } else {
-      const int64_t idx = (row0 + g) * a.max_parts + part;
-      a.ws_o[idx * D + d] = o;
-      if (d == 0) {
-        a.ws_m[idx] = bad ? qnan : s_m[g];
-        a.ws_l[idx] = bad ? qnan : l;
+    for (int g = 0; g < GT; ++g) {
+      m[g] = -INFINITY;
+      l[g] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < DL; ++e) acc[g][e] = 0.0f;
+    }
+    piece_bad = false;
+    if (cc.t == 0 && lane == 0)  // this wave starts the segment: record who holds its pieces
+      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wave_of(cc.gstart + cc.nt - 1));
+  };
+
+  // scores, softmax update and P.V for one tile with cn valid tokens
+  auto consume = [&](int cn, const u32x4 (&kb)[RK][NL], u32x4 (&vb)[RK][NL]) {
+    bool valid[RK];
+    const bool full = cn >= TK;  // wave-uniform
+#pragma unroll
+    for (int r = 0; r < RK; ++r) valid[r] = full || (r * GR + grp < cn);
+    if (!full) {  // rows past the context: their V (poison or block 0) must not reach acc
+#pragma unroll
+      for (int r = 0; r < RK; ++r)
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+          if (!valid[r]) vb[r][j] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      float sc[RK];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < RK; ++r) {
+        float d = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) d = dot16<T>(qv[g][j], kb[r][j], d);
+        sc[r] = group_sum<C>(d) * a.scale_log2;
+        mt = fmaxf(mt, valid[r] ? sc[r] : -INFINITY);
+      }
+      const float m_new = fmaxf(m[g], mt);
+      // Rescale only when some lane's running max grew; otherwise the factor is
+      // exp2(0) = 1 exactly in every lane and skipping it changes nothing.
+      if (__builtin_amdgcn_ballot_w64(m_new != m[g]) != 0) {
+        const float corr = rescale(m[g], m_new);
+        l[g] *= corr;
+#pragma unroll
+        for (int e = 0; e < DL; ++e) acc[g][e] *= corr;
+      }
+      m[g] = m_new;
+#pragma unroll
+      for (int r = 0; r < RK; ++r) {
+        const float p = valid[r] ? __builtin_amdgcn_exp2f(sc[r] - m_new) : 0.0f;
+        l[g] += p;
+        PV<T>::template run<NL>(acc[g], p, vb[r]);
       }
     }
+  };
+
+  // fold another token group's running state (max mo, sum lo, output acco) into row g
+  auto merge_state = [&](int g, float mo, float lo, const float* acco) {
+    const float mm = fmaxf(m[g], mo);
+    const float ca = rescale(m[g], mm);
+    const float cb = rescale(mo, mm);
+    l[g] = l[g] * ca + lo * cb;
+#pragma unroll
+    for (int e = 0; e < DL; ++e) acc[g][e] = acc[g][e] * ca + acco[e] * cb;
+    m[g] = mm;
+  };
+  // the same across a row-swap permute, which hands every lane both halves' values
+  auto merge_swapped = [&](int g, bool use32) {
+    float lo_acc[DL], hi_acc[DL];
+#pragma unroll
+    for (int e = 0; e < DL; ++e) {
+      const auto ax = use32 ? __builtin_amdgcn_permlane32_swap(as_u(acc[g][e]), as_u(acc[g][e]), false, false)
+                            : __builtin_amdgcn_permlane16_swap(as_u(acc[g][e]), as_u(acc[g][e]), false, false);
+      lo_acc[e] = as_f(ax[0]);
+      hi_acc[e] = as_f(ax[1]);
+    }
+    const auto mx = use32 ? __builtin_amdgcn_permlane32_swap(as_u(m[g]), as_u(m[g]), false, false)
+                          : __builtin_amdgcn_permlane16_swap(as_u(m[g]), as_u(m[g]), false, false);
+    const auto lx = use32 ? __builtin_amdgcn_permlane32_swap(as_u(l[g]), as_u(l[g]), false, false)
+                          : __builtin_amdgcn_permlane16_swap(as_u(l[g]), as_u(l[g]), false, false);
+    m[g] = as_f(mx[0]);
+    l[g] = as_f(lx[0]);
+#pragma unroll
+    for (int e = 0; e < DL; ++e) acc[g][e] = lo_acc[e];
+    merge_state(g, as_f(mx[1]), as_f(lx[1]), hi_acc);
+  };
+
+  // finish the piece that ends with the current tile: merge the token groups, then
+  // write the rows (whole segment) or a piece record (segment shared with other waves)
+  auto piece_end = [&]() {
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if constexpr (C == 8) {  // the two token groups of each 16-lane row
+        float other[DL];
+#pragma unroll
+        for (int e = 0; e < DL; ++e) other[e] = dpp_f<0x128>(acc[g][e]);  // row_ror:8
+        merge_state(g, dpp_f<0x128>(m[g]), dpp_f<0x128>(l[g]), other);
+      }
+      merge_swapped(g, true);   // lanes i and i^32
+      merge_swapped(g, false);  // lanes i and i^16
+    }
+    // lanes 0..C-1 now hold the piece's state for their chunks of the row
+    if (grp != 0) return;
+    const bool whole = cc.gstart >= A && cc.gstart + cc.nt <= A_end;
+    const bool head = cc.gstart < A;  // the segment began in an earlier wave
+    const float qnan = __builtin_nanf("");
+    const int64_t row0 = static_cast<int64_t>(cc.s) * a.num_q_heads + h0;
+    const int rec = w * 2 + (head ? 0 : 1);
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      if (g >= ng) break;
+      const float inv = piece_bad ? qnan : 1.0f / l[g];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        float o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = acc[g][j * E + e] * inv;
+        const int col = (j * C + sub) * E;
+        if (whole) {
+          *reinterpret_cast<u32x4*>(static_cast<T*>(a.out) + (row0 + g) * D + col) = pack16<T>(o);
+        } else {
+          float* dst = a.rec_o + (static_cast<int64_t>(rec) * GT + g) * D + col;
+#pragma unroll
+          for (int e = 0; e < E; e += 4)
+            *reinterpret_cast<u32x4*>(dst + e) = pack16<float>(&o[e]);
+        }
+      }
+      if (!whole && sub == 0) {
+        a.rec_m[rec * GT + g] = piece_bad ? qnan : m[g];
+        a.rec_l[rec * GT + g] = piece_bad ? qnan : l[g];
+      }
+    }
+  };
+
+  auto process = [&](int i, const u32x4 (&kb)[RK][NL], u32x4 (&vb)[RK][NL], bool stage_bad) {
+    if (i == 0 || cc.t == 0) piece_start();
+    piece_bad |= stage_bad;
+    consume(min(TK, cc.ctx - cc.t * TK), kb, vb);
+    if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
+    advance(cc);
+  };
+
+  // ---- main loop: the fetch cursor runs two tiles ahead of the compute cursor; every
+  // round issues the same loads (phantom tiles past the share read block 0)
+  Cursor cf = cc;
+  u32x4 k0[RK][NL], v0[RK][NL], k1[RK][NL], v1[RK][NL];
+  bool fb0 = fetch(cf, 0 < n_my, 0);
+  advance(cf);
+  bool fb1 = fetch(cf, 1 < n_my, 1);
+  advance(cf);
+  unstage(0, k0, v0);
+  bool pb0 = fb0;
+  fb0 = fetch(cf, 2 < n_my, 0);
+  advance(cf);
+  for (int i = 0; i < n_my; i += 2) {
+    process(i, k0, v0, pb0);
+    unstage(1, k1, v1);
+    const bool pb1 = fb1;
+    fb1 = fetch(cf, i + 3 < n_my, 1);
+    advance(cf);
+    if (i + 1 < n_my) process(i + 1, k1, v1, pb1);
+    unstage(0, k0, v0);
+    pb0 = fb0;
+    fb0 = fetch(cf, i + 4 < n_my, 0);
+    advance(cf);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS at exit
 }
 
 // ---------------------------------------------------------------------------
-// decode, pass 2: merge the partitions of one (sequence, query head); thread d owns dim d
+// decode, pass 2: one wave per (sequence, query head).  Empty or invalid contexts get
+// their zero or NaN row here; a segment held whole by one wave was written by it; a
+// segment split over waves w0..w1 is merged from the tail record of w0 and the head
+// records of w0+1..w1, in that order.  Lane p holds piece p's (max, sum); the weights
+// go through LDS and each lane sums the pieces' outputs for its dims.
 // ---------------------------------------------------------------------------
 
-template <typename T, int D>
-__global__ __launch_bounds__(D) void pa_reduce_kernel(T* __restrict__ out,
-                                                      const float* __restrict__ ws_m,
-                                                      const float* __restrict__ ws_l,
-                                                      const float* __restrict__ ws_o,
-                                                      const int32_t* __restrict__ context_lens,
-                                                      int num_q_heads, int max_context_len,
-                                                      int partition_size, int max_parts) {
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(kWave) void pa_reduce_kernel(
+    T* __restrict__ out, const int2* __restrict__ seg_desc, const float* __restrict__ rec_m,
+    const float* __restrict__ rec_l, const float* __restrict__ rec_o,
+    const int32_t* __restrict__ context_lens, int num_q_heads, int group, int n_gtiles,
+    int max_context_len, int w_cap) {
+  constexpr int kDPL = D / kWave;  // dims per lane
+  __shared__ float s_w[kWave];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
-  const int d = threadIdx.x;
+  const int lane = threadIdx.x;
+  T* dst = out + (static_cast<int64_t>(s) * num_q_heads + h) * D;
   const int ctx = context_lens[s];
-  if (ctx <= 0 || ctx > max_context_len) return;  // pass 1 wrote zeros or NaN
-  const int nparts = (ctx + partition_size - 1) / partition_size;
-  if (nparts <= 1) return;  // pass 1 wrote the output directly
-  const int64_t base = (static_cast<int64_t>(s) * num_q_heads + h) * max_parts;
-  float big_m = -INFINITY;
-  for (int p = 0; p < nparts; ++p) big_m = fmaxf(big_m, ws_m[base + p]);
-  float num = 0.0f, den = 0.0f;
-  for (int p = 0; p < nparts; ++p) {
-    const float wgt = ws_l[base + p] * __builtin_amdgcn_exp2f(ws_m[base + p] - big_m);
-    den += wgt;
-    num = fmaf(wgt, ws_o[(base + p) * D + d], num);
+  if (ctx <= 0 || ctx > max_context_len) {  // nothing to attend over: zeros; invalid: NaN
+    const T fill = static_cast<T>(ctx == 0 ? 0.0f : __builtin_nanf(""));
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = fill;
+    return;
   }
-  out[(static_cast<int64_t>(s) * num_q_heads + h) * D + d] = static_cast<T>(num / den);
+  const int kvh = h / group;
+  const int gtile = (h - kvh * group) / GT;
+  const int g = h - kvh * group - gtile * GT;
+  const int n_units = (num_q_heads / group) * n_gtiles;
+  const int2 d = seg_desc[s * n_units + kvh * n_gtiles + gtile];
+  if (d.x == d.y) return;  // one wave held the whole segment and wrote the row
+  if (d.x < 0 || d.x > d.y || d.y >= w_cap) {  // not written by the stream kernel: no records
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(__builtin_nanf(""));
+    return;
+  }
+  const int npieces = d.y - d.x + 1;
+  auto rec_of = [&](int p) { return p == 0 ? d.x * 2 + 1 : (d.x + p) * 2; };
+  float big_m = -INFINITY, den = 0.0f;
+  float num[kDPL];
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) num[k] = 0.0f;
+  for (int p0 = 0; p0 < npieces; p0 += kWave) {
+    const int p = p0 + lane;
+    const int r = p < npieces ? rec_of(p) * GT + g : 0;
+    const float mp = p < npieces ? rec_m[r] : -INFINITY;
+    const float lp = p < npieces ? rec_l[r] : 0.0f;
+    const float m_new = fmaxf(big_m, wave_max(mp));
+    const float c_old = rescale(big_m, m_new);
+    const float wp = p < npieces ? lp * __builtin_amdgcn_exp2f(mp - m_new) : 0.0f;
+    den = den * c_old + wave_sum(wp);
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) num[k] *= c_old;
+    __syncthreads();  // the previous group's weights are consumed
+    s_w[lane] = wp;
+    __syncthreads();
+    const int cnt = min(kWave, npieces - p0);
+    for (int i = 0; i < cnt; ++i) {
+      const float wgt = s_w[i];
+      const float* o = rec_o + (static_cast<int64_t>(rec_of(p0 + i)) * GT + g) * D;
+#pragma unroll
+      for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, o[k * kWave + lane], num[k]);
+    }
+    big_m = m_new;
+  }
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(num[k] / den);
 }
 
 // ---------------------------------------------------------------------------
@@ -496,22 +743,42 @@ int check_common(int dtype, int head_dim, int block_size) {
   return PA_OK;
 }
 
-struct DecodeGeom {
-  int partition_size;  // effective (> 0)
-  int max_parts;
-  int gt;
-  int n_gtiles;
-  size_t ws_bytes;     // required workspace (0 when one partition covers every context)
-};
-
-int max_parts_for(int max_context_len, int partition_size) {
-  if (max_context_len <= 0) return 1;
-  return (max_context_len + partition_size - 1) / partition_size;
+int group_tile(int group) {  // query heads per wave: 1, 2, 4 or 8 (padded rows are masked)
+  return group >= 5 ? 8 : group >= 3 ? 4 : group;
 }
 
-size_t workspace_for(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim, int64_t max_parts) {
-  const size_t per = static_cast<size_t>(num_seqs * num_q_heads * max_parts) * sizeof(float);
-  return 2 * align256(per) + align256(per * static_cast<size_t>(head_dim));
+// Geometry shared by the size query, the stream launch and the reduce launch.
+struct Geom {
+  int gt = 1;        // query heads per unit
+  int n_gtiles = 1;  // units per kv head
+  int n_units = 1;   // segments per sequence
+  int w_cap = 1;     // waves the workspace has records for
+  size_t desc_bytes = 0, rec_ml_bytes = 0, rec_o_bytes = 0, ws_bytes = 0;
+};
+
+// Waves asked for by partition_size > 0: enough that no wave takes much more than
+// partition_size tokens of one unit (the batch holds at most S * units * max_ctx).
+int64_t waves_for_partition(int64_t num_seqs, int n_units, int max_context_len, int partition_size) {
+  if (partition_size <= 0) return 0;
+  return (num_seqs * n_units * static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+}
+
+Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+              int max_context_len, int partition_size) {
+  Geom g;
+  const int group = num_q_heads / num_kv_heads;
+  g.gt = group_tile(group);
+  g.n_gtiles = (group + g.gt - 1) / g.gt;
+  g.n_units = num_kv_heads * g.n_gtiles;
+  int64_t w = kMaxWaves;
+  const int64_t want = waves_for_partition(num_seqs, g.n_units, max_context_len, partition_size);
+  if (want > w) w = want;
+  g.w_cap = static_cast<int>(w > (1 << 28) ? (1 << 28) : w);
+  g.desc_bytes = align256(static_cast<size_t>(num_seqs) * g.n_units * 2 * sizeof(int));
+  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.gt * sizeof(float));
+  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.gt * head_dim * sizeof(float));
+  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
+  return g;
 }
 
 struct DecodeCall {
@@ -531,7 +798,7 @@ struct DecodeCall {
   hipStream_t stream;
 };
 
-int check_decode(const DecodeCall& c, DecodeGeom* g) {
+int check_decode(const DecodeCall& c, Geom* g) {
   int rc = check_common(c.dtype, c.head_dim, c.block_size);
   if (rc != PA_OK) return rc;
   if (c.num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", c.num_seqs);
@@ -548,22 +815,17 @@ int check_decode(const DecodeCall& c, DecodeGeom* g) {
   if (c.partition_size < 0 || c.partition_size % c.block_size != 0)
     return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of block_size %d",
                 c.partition_size, c.block_size);
-  const int group = c.num_q_heads / c.num_kv_heads;
-  g->gt = group >= 8 ? 8 : group >= 4 ? (group == 4 ? 4 : 8) : group >= 2 ? (group == 2 ? 2 : 4) : 1;
-  g->n_gtiles = (group + g->gt - 1) / g->gt;
-  if (static_cast<int64_t>(c.num_kv_heads) * g->n_gtiles > 65535)
-    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d too large for one launch", c.num_q_heads);
   if (c.num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", c.num_seqs);
-  if (c.partition_size > 0) {
-    g->partition_size = c.partition_size;
-    g->max_parts = max_parts_for(c.max_context_len, c.partition_size);
-  } else {
-    // one partition per sequence: its length is the largest context, rounded to a whole chunk
-    const int span = c.max_context_len > 0 ? c.max_context_len : 1;
-    g->partition_size = (span + kChunk - 1) / kChunk * kChunk;
-    g->max_parts = 1;
-  }
-  g->ws_bytes = g->max_parts > 1 ? workspace_for(c.num_seqs, c.num_q_heads, c.head_dim, g->max_parts) : 0;
+  *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size);
+  // tile counts are 32-bit in the kernel (a tile holds at least 8 tokens)
+  if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8) >
+      (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles");
+  if (c.num_blocks > (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks above 2^31 - 1");
+  if (static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.dtype == PA_F16 ? 2 : 4) >
+      (static_cast<int64_t>(1) << 32) - 1)
+    return fail(PA_ERR_INVALID_ARG, "one block of one layer exceeds 4 GiB");
   if (c.num_seqs == 0) return PA_OK;
   if (!c.out || !c.q || !c.k_cache || !c.v_cache || !c.block_tables || !c.context_lens)
     return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
@@ -571,32 +833,76 @@ int check_decode(const DecodeCall& c, DecodeGeom* g) {
     return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(c.block_tables, 4) || !aligned(c.context_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
-  if (g->ws_bytes > 0) {
-    if (!c.workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g->ws_bytes);
-    if (c.workspace_bytes < g->ws_bytes)
-      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.workspace_bytes, g->ws_bytes);
-    if (!aligned(c.workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  }
+  if (!c.workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g->ws_bytes);
+  if (c.workspace_bytes < g->ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.workspace_bytes, g->ws_bytes);
+  if (!aligned(c.workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   return PA_OK;
 }
 
-void split_workspace(const DecodeCall& c, const DecodeGeom& g, float** m, float** l, float** o) {
-  if (g.ws_bytes == 0) {
-    *m = *l = *o = nullptr;
-    return;
+struct WsParts {
+  int2* desc;
+  float* rec_m;
+  float* rec_l;
+  float* rec_o;
+};
+
+WsParts split_workspace(void* ws, const Geom& g) {
+  char* b = static_cast<char*>(ws);
+  WsParts p;
+  p.desc = reinterpret_cast<int2*>(b);
+  p.rec_m = reinterpret_cast<float*>(b + g.desc_bytes);
+  p.rec_l = reinterpret_cast<float*>(b + g.desc_bytes + g.rec_ml_bytes);
+  p.rec_o = reinterpret_cast<float*>(b + g.desc_bytes + 2 * g.rec_ml_bytes);
+  return p;
+}
+
+// Resident one-wave work-groups of a kernel on the current device (cached per device
+// and kernel; the answer is fixed for a given build and device).
+template <typename T, int D, int GT>
+int resident_waves() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return kMaxWaves;
   }
-  const size_t per = static_cast<size_t>(c.num_seqs) * c.num_q_heads * g.max_parts * sizeof(float);
-  char* base = static_cast<char*>(c.workspace);
-  *m = reinterpret_cast<float*>(base);
-  *l = reinterpret_cast<float*>(base + align256(per));
-  *o = reinterpret_cast<float*>(base + 2 * align256(per));
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_stream_kernel<T, D, GT>, kWave, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        per_cu <= 0 || cus <= 0) {
+      (void)hipGetLastError();
+      return kMaxWaves;
+    }
+    cache[dev] = per_cu * cus;
+  }
+  return cache[dev];
+}
+
+// Waves of one launch: the resident count (at most kMaxWaves), raised with
+// partition_size > 0; never more than the workspace has records for.
+template <typename T, int D, int GT>
+int waves_for(const DecodeCall& c, const Geom& g) {
+  int64_t w = resident_waves<T, D, GT>();
+  if (w > kMaxWaves) w = kMaxWaves;
+  const int64_t want = waves_for_partition(c.num_seqs, g.n_units, c.max_context_len, c.partition_size);
+  if (want > w) w = want;
+  if (w > g.w_cap) w = g.w_cap;
+  return static_cast<int>(w < 1 ? 1 : w);
 }
 
 template <typename T, int D, int GT>
-int launch_partition(const DecodeCall& c, const DecodeGeom& g) {
-  PartitionArgs a;
+int launch_stream(const DecodeCall& c, const Geom& g) {
+  const WsParts ws = split_workspace(c.workspace, g);
+  StreamArgs a;
   a.out = c.out;
-  split_workspace(c, g, &a.ws_m, &a.ws_l, &a.ws_o);
+  a.seg_desc = ws.desc;
+  a.rec_m = ws.rec_m;
+  a.rec_l = ws.rec_l;
+  a.rec_o = ws.rec_o;
   a.q = c.q;
   a.k_cache = c.k_cache;
   a.v_cache = c.v_cache;
@@ -609,57 +915,43 @@ int launch_partition(const DecodeCall& c, const DecodeGeom& g) {
   a.num_q_heads = c.num_q_heads;
   a.group = c.num_q_heads / c.num_kv_heads;
   a.n_gtiles = g.n_gtiles;
+  a.n_units = g.n_units;
+  a.num_seqs = c.num_seqs;
   a.max_blocks_per_seq = c.max_blocks_per_seq;
   a.max_context_len = c.max_context_len;
   a.num_blocks = c.num_blocks;
-  a.partition_size = g.partition_size;
-  a.max_parts = g.max_parts;
-  const dim3 grid(g.max_parts, c.num_kv_heads * g.n_gtiles, c.num_seqs);
-  hipLaunchKernelGGL((pa_partition_kernel<T, D, GT>), grid, dim3(kThreads), 0, c.stream, a);
-  return check_hip("pa_partition_kernel launch");
+  a.num_waves = waves_for<T, D, GT>(c, g);
+  hipLaunchKernelGGL((pa_stream_kernel<T, D, GT>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  return check_hip("pa_stream_kernel launch");
 }
 
-template <typename T, int D>
-int launch_partition_gt(const DecodeCall& c, const DecodeGeom& g) {
-  switch (g.gt) {
-    case 1: return launch_partition<T, D, 1>(c, g);
-    case 2: return launch_partition<T, D, 2>(c, g);
-    case 4: return launch_partition<T, D, 4>(c, g);
-    default: return launch_partition<T, D, 8>(c, g);
-  }
-}
-
-int run_partitions(const DecodeCall& c, const DecodeGeom& g) {
-  if (c.num_seqs == 0) return PA_OK;
-  if (c.dtype == PA_F16)
-    return c.head_dim == 64 ? launch_partition_gt<f16, 64>(c, g) : launch_partition_gt<f16, 128>(c, g);
-  return c.head_dim == 64 ? launch_partition_gt<float, 64>(c, g) : launch_partition_gt<float, 128>(c, g);
-}
-
-template <typename T, int D>
-int launch_reduce(void* out, const float* m, const float* l, const float* o, const int32_t* ctx,
-                  int num_seqs, int num_q_heads, int max_context_len, int partition_size,
-                  int max_parts, hipStream_t stream) {
-  const dim3 grid(num_q_heads, num_seqs);
-  hipLaunchKernelGGL((pa_reduce_kernel<T, D>), grid, dim3(D), 0, stream, static_cast<T*>(out), m,
-                     l, o, ctx, num_q_heads, max_context_len, partition_size, max_parts);
+template <typename T, int D, int GT>
+int launch_reduce(const DecodeCall& c, const Geom& g) {
+  const WsParts ws = split_workspace(c.workspace, g);
+  hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
+                     c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
+                     c.context_lens, c.num_q_heads, c.num_q_heads / c.num_kv_heads, g.n_gtiles,
+                     c.max_context_len, g.w_cap);
   return check_hip("pa_reduce_kernel launch");
 }
 
-int run_reduce(void* out, const int32_t* ctx, int num_seqs, int num_q_heads, int head_dim,
-               int max_context_len, int dtype, const DecodeGeom& g, const void* workspace,
-               hipStream_t stream) {
-  if (num_seqs == 0 || g.max_parts <= 1) return PA_OK;
-  const size_t per = static_cast<size_t>(num_seqs) * num_q_heads * g.max_parts * sizeof(float);
-  const char* base = static_cast<const char*>(workspace);
-  const float* m = reinterpret_cast<const float*>(base);
-  const float* l = reinterpret_cast<const float*>(base + align256(per));
-  const float* o = reinterpret_cast<const float*>(base + 2 * align256(per));
-  if (dtype == PA_F16)
-    return head_dim == 64 ? launch_reduce<f16, 64>(out, m, l, o, ctx, num_seqs, num_q_heads, max_context_len, g.partition_size, g.max_parts, stream)
-                          : launch_reduce<f16, 128>(out, m, l, o, ctx, num_seqs, num_q_heads, max_context_len, g.partition_size, g.max_parts, stream);
-  return head_dim == 64 ? launch_reduce<float, 64>(out, m, l, o, ctx, num_seqs, num_q_heads, max_context_len, g.partition_size, g.max_parts, stream)
-                        : launch_reduce<float, 128>(out, m, l, o, ctx, num_seqs, num_q_heads, max_context_len, g.partition_size, g.max_parts, stream);
+template <int Which, typename T, int D>
+int dispatch_gt(const DecodeCall& c, const Geom& g) {
+  switch (g.gt) {
+    case 1: return Which == 0 ? launch_stream<T, D, 1>(c, g) : launch_reduce<T, D, 1>(c, g);
+    case 2: return Which == 0 ? launch_stream<T, D, 2>(c, g) : launch_reduce<T, D, 2>(c, g);
+    case 4: return Which == 0 ? launch_stream<T, D, 4>(c, g) : launch_reduce<T, D, 4>(c, g);
+    default: return Which == 0 ? launch_stream<T, D, 8>(c, g) : launch_reduce<T, D, 8>(c, g);
+  }
+}
+
+// Which = 0: the stream kernel; 1: the reduce kernel
+template <int Which>
+int dispatch(const DecodeCall& c, const Geom& g) {
+  if (c.num_seqs == 0) return PA_OK;
+  if (c.dtype == PA_F16)
+    return c.head_dim == 64 ? dispatch_gt<Which, f16, 64>(c, g) : dispatch_gt<Which, f16, 128>(c, g);
+  return c.head_dim == 64 ? dispatch_gt<Which, float, 64>(c, g) : dispatch_gt<Which, float, 128>(c, g);
 }
 
 template <typename T, int D>
@@ -740,13 +1032,12 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping, vo
                         : launch_cache_write<float, 128>(k, v, slot_mapping, k_cache, v_cache, num_tokens, num_kv_heads, block_size, num_blocks, st);
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size <= 0)
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      max_context_len < 0 || partition_size < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  const int max_parts = max_parts_for(max_context_len, partition_size);
-  if (max_parts <= 1) return 0;
-  return workspace_for(num_seqs, num_q_heads, head_dim, max_parts);
+  return geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size).ws_bytes;
 }
 
 int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -760,36 +1051,46 @@ int pa_decode_partitions(void* out, const void* q, const void* k_cache, const vo
                                  block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
                                  max_blocks_per_seq, max_context_len, num_blocks, partition_size,
                                  dtype, workspace, workspace_bytes, stream);
-  DecodeGeom g;
+  Geom g;
   const int rc = check_decode(c, &g);
   if (rc != PA_OK) return rc;
-  return run_partitions(c, g);
+  return dispatch<0>(c, g);
 }
 
 int pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
-                     int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
-                     int32_t partition_size, int32_t dtype, const void* workspace,
-                     size_t workspace_bytes, void* stream) {
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t max_context_len, int32_t partition_size, int32_t dtype,
+                     const void* workspace, size_t workspace_bytes, void* stream) {
   g_error.clear();
   if (dtype != PA_F32 && dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "dtype %d is not PA_F32 or PA_F16", dtype);
   if (head_dim != 64 && head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d: only 64 and 128 are built", head_dim);
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0 || partition_size < 0)
-    return fail(PA_ERR_INVALID_ARG, "negative size");
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
-  if (partition_size == 0 || num_seqs == 0) return PA_OK;
-  DecodeGeom g;
-  g.partition_size = partition_size;
-  g.max_parts = max_parts_for(max_context_len, partition_size);
-  g.ws_bytes = g.max_parts > 1 ? workspace_for(num_seqs, num_q_heads, head_dim, g.max_parts) : 0;
-  if (g.ws_bytes == 0) return PA_OK;
+  if (num_seqs == 0) return PA_OK;
+  const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(out, 16) || !aligned(context_lens, 4)) return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);
   if (workspace_bytes < g.ws_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, g.ws_bytes);
   if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  return run_reduce(out, context_lens, num_seqs, num_q_heads, head_dim, max_context_len, dtype, g,
-                    workspace, static_cast<hipStream_t>(stream));
+  DecodeCall c{};
+  c.out = out;
+  c.context_lens = context_lens;
+  c.num_seqs = num_seqs;
+  c.num_q_heads = num_q_heads;
+  c.num_kv_heads = num_kv_heads;
+  c.head_dim = head_dim;
+  c.max_context_len = max_context_len;
+  c.partition_size = partition_size;
+  c.dtype = dtype;
+  c.workspace = const_cast<void*>(workspace);
+  c.workspace_bytes = workspace_bytes;
+  c.stream = static_cast<hipStream_t>(stream);
+  return dispatch<1>(c, g);
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -803,13 +1104,12 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
                                  block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
                                  max_blocks_per_seq, max_context_len, num_blocks, partition_size,
                                  dtype, workspace, workspace_bytes, stream);
-  DecodeGeom g;
+  Geom g;
   int rc = check_decode(c, &g);
   if (rc != PA_OK) return rc;
-  rc = run_partitions(c, g);
+  rc = dispatch<0>(c, g);
   if (rc != PA_OK) return rc;
-  return run_reduce(out, context_lens, num_seqs, num_q_heads, head_dim, max_context_len, dtype, g,
-                    workspace, c.stream);
+  return dispatch<1>(c, g);
 }
 
 }  // extern "C"

@@ -58,7 +58,8 @@ def decode(case, d, partition_size=P.DEFAULT_PARTITION, max_context_len=None, q=
             d.ctx if ctx is None else ctx, case.scale, case.block_size, case.num_kv_heads)
     if split:
         ws = P.pa_decode_partitions(*args, max_context_len=mcl, partition_size=partition_size)
-        P.pa_decode_reduce(out, d.ctx if ctx is None else ctx, mcl, partition_size, ws)
+        P.pa_decode_reduce(out, d.ctx if ctx is None else ctx, case.num_kv_heads, mcl,
+                           partition_size, ws)
     else:
         P.pa_decode(*args, max_context_len=mcl, partition_size=partition_size)
     torch.cuda.synchronize()

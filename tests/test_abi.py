@@ -37,16 +37,26 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (1 << 16)
+    assert P.lib().pa_abi_version() == (2 << 16)
 
 
 def test_workspace_size_query():
-    # 64 seqs x 32 heads x 8 partitions: m and l (fp32) plus 128-dim outputs
-    per = 64 * 32 * 8 * 4
-    assert P.pa_decode_workspace_bytes(64, 32, 128, 4096, 512) == 2 * per + per * 128
-    assert P.pa_decode_workspace_bytes(64, 32, 128, 4096, 0) == 0
-    assert P.pa_decode_workspace_bytes(64, 32, 128, 512, 512) == 0  # one partition: none needed
-    assert P.pa_decode_workspace_bytes(0, 32, 128, 4096, 512) == 0
+    # per (sequence, unit) a 2-int descriptor; per wave two records of GT rows:
+    # fp32 max and sum (each region 256-byte aligned) and GT * head_dim fp32 outputs
+    al = lambda x: (x + 255) // 256 * 256
+    S, hq, hkv, d = 64, 32, 8, 128  # group 4: one unit of 4 rows per kv head
+    waves = 4096
+    want = al(S * hkv * 8) + 2 * al(2 * waves * 4 * 4) + al(2 * waves * 4 * d * 4)
+    assert P.pa_decode_workspace_bytes(S, hq, hkv, d, 4096, 0) == want
+    # 56 query / 8 kv heads: groups of 7 padded to 8 rows
+    want7 = al(8 * 8 * 8) + 2 * al(2 * waves * 8 * 4) + al(2 * waves * 8 * d * 4)
+    assert P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 0) == want7
+    # a partition size asks for more waves once the batch exceeds 4096 of them
+    big = P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 512)
+    waves_p = (8 * 8 * 131072 + 511) // 512
+    assert big == al(8 * 8 * 8) + 2 * al(2 * waves_p * 8 * 4) + al(2 * waves_p * 8 * d * 4)
+    assert P.pa_decode_workspace_bytes(0, hq, hkv, d, 4096, 0) == 0
+    assert P.pa_decode_workspace_bytes(4, 30, 8, d, 4096, 0) == 0  # 30 % 8 != 0
 
 
 FAKE = 1 << 20  # a 16-byte aligned non-null address that is never dereferenced
@@ -116,11 +126,13 @@ def test_cache_write_with_no_tokens_is_a_no_op():
 
 def test_reduce_rejects_bad_arguments():
     lib = P.lib()
-    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 96, 4096, 512, 1, FAKE, 1 << 30, None) == \
+    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 8, 96, 4096, 0, 1, FAKE, 1 << 30, None) == \
         _lib.PA_ERR_UNSUPPORTED
-    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 128, 4096, 512, 1, None, 0, None) == \
+    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 4096, 0, 1, None, 0, None) == \
         _lib.PA_ERR_WORKSPACE
-    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 128, 4096, 0, 1, None, 0, None) == _lib.PA_OK
+    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 30, 8, 128, 4096, 0, 1, FAKE, 1 << 30, None) == \
+        _lib.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_reduce(FAKE, FAKE, 0, 32, 8, 128, 4096, 0, 1, None, 0, None) == _lib.PA_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -2,7 +2,10 @@
 
 Writes must match byte for byte; attention must be within |d| <= 2e-3 + 1e-2|ref|
 and the normalised error bound.  Exact invariants (physical relabelling, context 1,
-duplicated rows, padding poison, block size) are checked bitwise on the GPU.
+padding poison, block size, split launches, repeat runs) are checked bitwise on the
+GPU.  Where a context is cut between waves depends on the whole batch, so the same
+sequence at another batch position (duplicated rows, a changed neighbour) is checked
+to within one rounding of the output type.
 """
 import functools
 
@@ -65,11 +68,11 @@ def _config(name, variant):
 
 CONFIG_RUNS = [
     ("tiny_fp32", "plain", 64), ("tiny_fp32", "needle", 64), ("tiny_fp32", "poscode", 0),
-    ("llama3_8b", "plain", 512), ("llama3_8b", "needle", 256), ("llama3_8b", "poscode", 512),
-    ("llama2_70b", "plain", 512), ("llama2_70b", "needle", 512),
-    ("shared_prefix", "plain", 512), ("shared_prefix", "needle", 512),
-    ("shared_prefix", "poscode", 512),
-    ("long_context_b16", "plain", 512), ("long_context_b16", "needle", 512),
+    ("llama3_8b", "plain", 0), ("llama3_8b", "needle", 256), ("llama3_8b", "poscode", 512),
+    ("llama2_70b", "plain", 0), ("llama2_70b", "needle", 512),
+    ("shared_prefix", "plain", 0), ("shared_prefix", "needle", 512),
+    ("shared_prefix", "poscode", 0),
+    ("long_context_b16", "plain", 0), ("long_context_b16", "needle", 512),
 ]
 
 
@@ -162,7 +165,23 @@ def test_context_one_returns_v_exactly(dtype):
             assert got[s, h].tobytes() == case.new_v[s, h // 4].tobytes()
 
 
-def test_duplicated_rows_bit_identical():
+def _within_one_rounding(a, b, dtype, label):
+    """fp16: at most one unit in the last place apart; fp32: relative 1e-5."""
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b)), label
+    if np.dtype(dtype) == np.float16:
+        def ordered(x):
+            u = x.astype(np.float16).view(np.uint16).astype(np.int32)
+            return np.where(u & 0x8000, -(u & 0x7FFF), u)
+        dist = np.abs(ordered(a) - ordered(b))
+        assert dist.max() <= 1, f"{label}: {dist.max()} ulp apart"
+    else:
+        a64, b64 = a.astype(np.float64), b.astype(np.float64)
+        assert np.all(np.abs(a64 - b64) <= 1e-5 * np.abs(b64) + 1e-7), label
+
+
+def test_duplicated_rows_within_rounding():
     torch = _torch()
     case = _mid_case()
     d = G.to_device(case)
@@ -171,12 +190,14 @@ def test_duplicated_rows_bit_identical():
     bt = d.tables[idx].contiguous()
     ctx = d.ctx[idx].contiguous()
     got = G.decode(case, d, q=q, tables=bt, ctx=ctx)
-    assert got[0].tobytes() == got[2].tobytes() == got[4].tobytes()
+    _within_one_rounding(got[0], got[2], case.dtype, "copy 2")
+    _within_one_rounding(got[0], got[4], case.dtype, "copy 4")
     full = G.decode(case, d)
-    assert got[0].tobytes() == full[5].tobytes() and got[1].tobytes() == full[0].tobytes()
+    _within_one_rounding(got[0], full[5], case.dtype, "seq 5")
+    _within_one_rounding(got[1], full[0], case.dtype, "seq 0")
 
 
-def test_shared_prompt_blocks_identical_for_identical_queries():
+def test_shared_prompt_blocks_agree_for_identical_queries():
     torch = _torch()
     case = _config("shared_prefix", "plain")
     d = G.to_device(case)
@@ -186,7 +207,7 @@ def test_shared_prompt_blocks_identical_for_identical_queries():
     ctx = torch.full((8,), 2000, dtype=torch.int32, device="cuda")
     got = G.decode(case, d, q=q.contiguous(), tables=d.tables[:8].contiguous(), ctx=ctx)
     for s in range(1, 8):
-        assert got[s].tobytes() == got[0].tobytes()
+        _within_one_rounding(got[s], got[0], case.dtype, f"sample {s}")
 
 
 def test_padding_poison_has_no_effect():
@@ -250,7 +271,7 @@ def test_context_zero_gives_zero_rows():
     assert np.all(got[2] == 0)
     full = G.decode(case, d)
     keep = [0, 1, 3, 4, 5]
-    assert got[keep].tobytes() == full[keep].tobytes()
+    _within_one_rounding(got[keep], full[keep], case.dtype, "other rows")
 
 
 def test_no_sequences_is_a_no_op():
