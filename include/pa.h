@@ -108,12 +108,16 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * that many tokens at most.  Results are bitwise identical under any relabelling of
  * physical blocks and any block size; where a context is split depends on the whole
  * batch, so the same sequence at another batch position may differ in rounding.
+ * Arithmetic: fp32 scores, softmax and accumulation.  For PA_F16 the probabilities are
+ * rounded to fp16 for the P.V product (on the matrix cores), which bounds the output's
+ * deviation from exact attention by about 2^-11 * (|out| + max |v|).
  *
  * out                device, [num_seqs, num_q_heads, head_dim], dtype; written
  * q                  device, [num_seqs, num_q_heads, head_dim], dtype
  * k_cache, v_cache   device, [num_blocks, num_kv_heads, block_size, head_dim], dtype
  * block_tables       device, [num_seqs, max_blocks_per_seq] int32
  * context_lens       device, [num_seqs] int32
+ * scale              softmax scale (1/sqrt(head_dim) on the pages); positive and finite
  * max_context_len    host bound on every context_lens[s]; at most max_blocks_per_seq * block_size
  * workspace          device, >= pa_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                    contents need no initialisation and are scratch between calls

@@ -43,11 +43,14 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <type_traits>
+#include <utility>
 
 #include "pa.h"
 
@@ -58,7 +61,9 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
-constexpr int kMaxWaves = 4096;  // persistent waves in the default split (MI355X holds 2048+)
+constexpr int kMaxWaves = 4096;  // persistent fp32 waves in the default split
+constexpr int kMfWavesPerCU = 4;  // persistent fp16 waves per compute unit in the default split
+constexpr int kMfStages = 3;      // LDS ring depth of the fp16 kernel
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -199,6 +204,21 @@ __device__ __forceinline__ float rescale(float a, float b) {
   return a == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(a - b);
 }
 
+// A wave-uniform 32-bit load through the scalar unit (the address is in SGPRs).  Its
+// completion is tracked by lgkmcnt, so waiting for it never waits for the K/V loads in
+// flight.  Written as asm because the compiler emits a vector load (and a wait for every
+// outstanding vector load) wherever it cannot prove the memory unmodified since entry.
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
+  // readfirstlane keeps the address in SGPRs even where the compiler computed it in VGPRs
+  const uint64_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  const int32_t* q = reinterpret_cast<const int32_t*>((static_cast<uint64_t>(hi) << 32) | lo);
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(q));
+  return v;
+}
+
 // Read one ring stage back: wait until at most VMCNT vector-memory operations are
 // outstanding (the stage's own direct-to-LDS loads are older than those, and loads
 // complete in order), then read the lane's eight 16-byte words at base + 16*lane +
@@ -324,6 +344,77 @@ struct Cursor {
   int gstart;  // global index of the segment's first tile
 };
 
+// The batch as one list of tiles (TK consecutive tokens of one segment, segments in
+// order), and one wave's equal share of it.  Every member is wave-uniform.
+template <int TK>
+struct Work {
+  const int32_t* ctxs;
+  int S, max_ctx, n_units;
+  int Q, R;     // every wave takes Q tiles, the first R waves one more
+  int A, n_my;  // this wave's share: tiles [A, A + n_my)
+
+  __device__ int seg_tiles(int ctx) const {  // invalid or empty contexts contribute no tiles
+    return (ctx > 0 && ctx <= max_ctx) ? (ctx + TK - 1) / TK : 0;
+  }
+
+  __device__ void init(const StreamArgs& a, int w, int lane) {
+    ctxs = a.context_lens;
+    S = a.num_seqs;
+    max_ctx = a.max_context_len;
+    n_units = a.n_units;
+    int part = 0;
+    for (int b = 0; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
+    const int total = wave_sum_int(part) * n_units;
+    Q = total / a.num_waves;
+    R = total - Q * a.num_waves;
+    A = w * Q + min(w, R);
+    n_my = Q + (w < R ? 1 : 0);
+  }
+
+  __device__ int wave_of(int x) const {  // the wave whose share holds global tile x
+    const int cut = R * (Q + 1);
+    return (x < cut || Q == 0) ? x / (Q + 1) : R + (x - cut) / Q;
+  }
+
+  // Cursor at tile A: scan the per-sequence tile counts for the sequence covering it.
+  __device__ Cursor locate(int lane) const {
+    int s0 = 0, base = 0;  // base: global index of s0's first tile
+    for (int b = 0; b < S; b += kWave) {
+      const int ts = ((b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0) * n_units;
+      const int incl = wave_incl_scan_int(ts, lane);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > A);
+      if (hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        s0 = b + l;
+        base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
+        break;
+      }
+      base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    Cursor c;
+    c.s = s0;
+    c.ctx = scalar_load(ctxs + s0);
+    c.nt = seg_tiles(c.ctx);
+    c.unit = (A - base) / c.nt;
+    c.t = (A - base) - c.unit * c.nt;
+    c.gstart = base + c.unit * c.nt;
+    return c;
+  }
+
+  __device__ void advance(Cursor& c) const {
+    if (++c.t < c.nt) return;
+    c.gstart += c.nt;
+    c.t = 0;
+    if (++c.unit < n_units) return;
+    c.unit = 0;
+    do {
+      ++c.s;
+      c.ctx = c.s < S ? scalar_load(ctxs + c.s) : 0;
+      c.nt = seg_tiles(c.ctx);
+    } while (c.nt == 0 && c.s < S);
+  }
+};
+
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   using K = Cfg<T, D, GT>;
@@ -336,60 +427,15 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   const int lane = threadIdx.x;
   const int sub = lane % C;  // which chunks of a row this lane holds
   const int grp = lane / C;  // which token of a row slot this lane holds
-  const int S = a.num_seqs;
-  const int32_t* ctxs = a.context_lens;
-  auto seg_tiles = [&](int ctx) {  // invalid or empty contexts contribute no tiles
-    return (ctx > 0 && ctx <= a.max_context_len) ? (ctx + TK - 1) / TK : 0;
-  };
 
-  // ---- total tiles and this wave's share [A, A + n_my)
-  int part = 0;
-  for (int b = 0; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
-  const int total = wave_sum_int(part) * a.n_units;
-  const int W = a.num_waves;
-  const int Q = total / W, R = total - (total / W) * W;
-  const int A = w * Q + min(w, R);
-  const int n_my = Q + (w < R ? 1 : 0);
+  // ---- this wave's share of the batch's tiles, and the cursor at its first tile
+  Work<TK> wk;
+  wk.init(a, w, lane);
+  const int n_my = wk.n_my;
   if (n_my == 0) return;
-  const int A_end = A + n_my;
-  auto wave_of = [&](int x) {  // owner of global tile x
-    const int cut = R * (Q + 1);
-    return x < cut ? x / (Q + 1) : R + (x - cut) / Q;
-  };
-
-  // ---- locate tile A: the sequence whose tiles cover it
-  int s0 = 0, base = 0;  // base: global index of s0's first tile
-  for (int b = 0; b < S; b += kWave) {
-    const int ts = ((b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0) * a.n_units;
-    const int incl = wave_incl_scan_int(ts, lane);
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > A);
-    if (hit != 0) {
-      const int l = __builtin_ctzll(hit);
-      s0 = b + l;
-      base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
-      break;
-    }
-    base += __builtin_amdgcn_readlane(incl, kWave - 1);
-  }
-  Cursor cc;  // the tile being computed
-  cc.s = s0;
-  cc.ctx = ctxs[s0];
-  cc.nt = seg_tiles(cc.ctx);
-  cc.unit = (A - base) / cc.nt;
-  cc.t = (A - base) - cc.unit * cc.nt;
-  cc.gstart = base + cc.unit * cc.nt;
-  auto advance = [&](Cursor& c) {
-    if (++c.t < c.nt) return;
-    c.gstart += c.nt;
-    c.t = 0;
-    if (++c.unit < a.n_units) return;
-    c.unit = 0;
-    do {
-      ++c.s;
-      c.ctx = c.s < S ? ctxs[c.s] : 0;
-      c.nt = seg_tiles(c.ctx);
-    } while (c.nt == 0 && c.s < S);
-  };
+  const int A = wk.A, A_end = A + n_my;
+  Cursor cc = wk.locate(lane);  // the tile being computed
+  auto advance = [&](Cursor& c) { wk.advance(c); };
 
   // ---- direct-to-LDS loads of one tile into a ring stage
   const char* kcache = static_cast<const char*>(a.k_cache);
@@ -404,12 +450,17 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     bool bad = false;
     const int kvh = real ? f.unit / a.n_gtiles : 0;
     const int32_t* trow = a.block_tables + static_cast<int64_t>(real ? f.s : 0) * a.max_blocks_per_seq;
+    int p = 0, p_idx = -1;  // table entry of the previous row slot and its index
 #pragma unroll
     for (int r = 0; r < RK; ++r) {
       const int tok0 = f.t * TK + r * GR;  // first token of the row slot (wave-uniform)
-      int p = 0;
-      if (real && tok0 < f.ctx) {
-        p = trow[tok0 >> a.log2_block];  // scalar load
+      const int idx = tok0 >> a.log2_block;
+      if (!(real && tok0 < f.ctx)) {
+        p = 0;
+        p_idx = -1;
+      } else if (idx != p_idx) {  // row slots of one block share the entry
+        p = scalar_load(trow + idx);
+        p_idx = idx;
         if (p < 0 || p >= a.num_blocks) {
           bad = true;
           p = 0;
@@ -472,11 +523,21 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     }
     piece_bad = false;
     if (cc.t == 0 && lane == 0)  // this wave starts the segment: record who holds its pieces
-      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wave_of(cc.gstart + cc.nt - 1));
+      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+    // Wait for the q rows here, once per piece.  Left to the compiler, the wait lands at
+    // the first use of q on every tile (it cannot tell whether this branch ran) and would
+    // drain the K/V loads in flight each time.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   };
 
-  // scores, softmax update and P.V for one tile with cn valid tokens
+  // Scores, softmax update and P.V for one tile with cn valid tokens.  Scores stay in
+  // raw dot-product units; the probability of score x is exp2(x * scale_log2 - m), with
+  // m the piece's reference (log2 units).  The reference is raised only when a score
+  // would exceed it by more than kRebase: the probabilities then stay below 2^kRebase,
+  // far from overflow, and the costly rescale of the accumulators is rare.  Any
+  // reference gives the same result, because every merge rescales by the stored one.
   auto consume = [&](int cn, const u32x4 (&kb)[RK][NL], u32x4 (&vb)[RK][NL]) {
+    constexpr float kRebase = 8.0f;
     bool valid[RK];
     const bool full = cn >= TK;  // wave-uniform
 #pragma unroll
@@ -488,35 +549,45 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
         for (int j = 0; j < NL; ++j)
           if (!valid[r]) vb[r][j] = u32x4{0u, 0u, 0u, 0u};
     }
+    float sc[GT][RK];
 #pragma unroll
-    for (int g = 0; g < GT; ++g) {
-      float sc[RK];
-      float mt = -INFINITY;
+    for (int g = 0; g < GT; ++g)
 #pragma unroll
       for (int r = 0; r < RK; ++r) {
         float d = 0.0f;
 #pragma unroll
         for (int j = 0; j < NL; ++j) d = dot16<T>(qv[g][j], kb[r][j], d);
-        sc[r] = group_sum<C>(d) * a.scale_log2;
-        mt = fmaxf(mt, valid[r] ? sc[r] : -INFINITY);
+        sc[g][r] = group_sum<C>(d);
       }
-      const float m_new = fmaxf(m[g], mt);
-      // Rescale only when some lane's running max grew; otherwise the factor is
-      // exp2(0) = 1 exactly in every lane and skipping it changes nothing.
-      if (__builtin_amdgcn_ballot_w64(m_new != m[g]) != 0) {
+    float mt[GT];
+    bool need = false;
+#pragma unroll
+    for (int g = 0; g < GT; ++g) {
+      mt[g] = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < RK; ++r) mt[g] = fmaxf(mt[g], valid[r] ? sc[g][r] : -INFINITY);
+      mt[g] *= a.scale_log2;  // scale > 0: the largest raw score gives the largest scaled one
+      need |= mt[g] > m[g] + kRebase;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int g = 0; g < GT; ++g) {
+        const float m_new = fmaxf(m[g], mt[g]);
         const float corr = rescale(m[g], m_new);
         l[g] *= corr;
 #pragma unroll
         for (int e = 0; e < DL; ++e) acc[g][e] *= corr;
+        m[g] = m_new;
       }
-      m[g] = m_new;
+    }
+#pragma unroll
+    for (int g = 0; g < GT; ++g)
 #pragma unroll
       for (int r = 0; r < RK; ++r) {
-        const float p = valid[r] ? __builtin_amdgcn_exp2f(sc[r] - m_new) : 0.0f;
+        const float p = valid[r] ? __builtin_amdgcn_exp2f(fmaf(sc[g][r], a.scale_log2, -m[g])) : 0.0f;
         l[g] += p;
         PV<T>::template run<NL>(acc[g], p, vb[r]);
       }
-    }
   };
 
   // fold another token group's running state (max mo, sum lo, output acco) into row g
@@ -633,6 +704,353 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// fp16 decode, pass 1, on the matrix cores
+//
+// Per tile of 16 tokens, with K and V staged in LDS:
+//   S^T = K Q^T       D/32 v_mfma_f32_16x16x32_f16: A = K (token x dims), B = Q^T
+//   O^T += V^T P^T    D/16 v_mfma_f32_16x16x16_f16: A = V^T (dims x token), B = P^T
+// The 16 columns of B are the query heads that share the kv head (a group of up to 16;
+// unused columns are zero).  Lane (g, j) = (lane % 16, lane / 16) gets scores of row g
+// for tokens 4j..4j+3, which is exactly the P^T operand layout of the second product,
+// and accumulates O[g][16 nb + 4j + i]: the softmax state of row g stays in the lanes
+// of row g.  V^T comes out of LDS through the transposing ds_read_b64_tr_b16.
+// ---------------------------------------------------------------------------
+
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMfRows = 16;  // query rows per wave: the N extent of both products
+
+template <int D>
+struct MCfg {
+  static constexpr int kRow = D * 2;           // bytes per K or V token row
+  static constexpr int kNC = kRow / 16;        // 16-byte chunks per row: 8 or 16
+  static constexpr int kTK = 16;               // tokens per tile
+  static constexpr int kHalf = kTK * kRow;     // bytes of K (or V) per tile
+  static constexpr int kLoads = kHalf / 1024;  // 1 KB direct-to-LDS loads for each of K and V
+  static constexpr int kKB = D / 32;           // products for the scores
+  static constexpr int kNB = D / 16;           // products for P.V
+  static constexpr int kStage = 2 * kHalf;     // one ring stage: the K tile, then the V tile
+  static constexpr int kRowsPerLoad = 64 / kNC;
+  static_assert(kLoads * kRowsPerLoad == kTK, "a load covers whole rows");
+};
+
+// Chunk c of token row r is stored at chunk position c ^ swz(r) of that row.  Over any 8
+// consecutive rows swz takes 8 distinct values, so the 8 lanes of one ds_read_b128 cycle
+// (rows 0-7 or 8-15, one chunk) hit distinct banks; over each aligned group of 4 rows
+// swz / 2 takes 4 distinct values, so the 16 lanes of one transposing read cycle (4 rows
+// x 2 chunks) do too.
+__device__ __forceinline__ int swz(int r) { return (2 * r + (r >> 2)) & 7; }
+
+// Read one ring stage's operands: wait until at most VM vector-memory operations are
+// outstanding (the stage's own loads are older), then the K operands (ds_read_b128) and
+// the V^T operands (ds_read_b64_tr_b16) at the lane's addresses + OFF, then wait for the
+// reads.  One asm block, so the compiler's conservative tracking of direct-to-LDS loads
+// cannot put a full drain in front of the reads.
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_d128(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                                f16x8 (&k)[4], f16x4 (&v)[8]) {
+  asm volatile(
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %0, %12 offset:%[off]\n\t"
+      "ds_read_b128 %1, %13 offset:%[off]\n\t"
+      "ds_read_b128 %2, %14 offset:%[off]\n\t"
+      "ds_read_b128 %3, %15 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %4, %16 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %6, %18 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %7, %19 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %8, %20 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %9, %21 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %10, %22 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %11, %23 offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3]), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]),
+        "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7])
+      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
+        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), [vm] "n"(VM), [off] "n"(OFF)
+      : "memory");
+}
+
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_d64(const uint32_t (&ka)[2], const uint32_t (&va)[4],
+                                               f16x8 (&k)[2], f16x4 (&v)[4]) {
+  asm volatile(
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %0, %6 offset:%[off]\n\t"
+      "ds_read_b128 %1, %7 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %4, %10 offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %5, %11 offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(k[0]), "=v"(k[1]), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3])
+      : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), [vm] "n"(VM),
+        [off] "n"(OFF)
+      : "memory");
+}
+
+template <int D, int VM, int OFF>
+__device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], const uint32_t (&va)[D / 16],
+                                              f16x8 (&k)[D / 32], f16x4 (&v)[D / 16]) {
+  if constexpr (D == 128) read_stage_d128<VM, OFF>(ka, va, k, v);
+  else read_stage_d64<VM, OFF>(ka, va, k, v);
+}
+
+// Call f(std::integral_constant<int, i>{}) for i = 0 .. N-1: a loop whose index is a
+// compile-time constant in the body (stage offsets become instruction immediates).
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll(F&& f) {
+  unroll_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <int D, int NST>
+__global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs a) {
+  using K = MCfg<D>;
+  constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
+  constexpr int LOADS = K::kLoads, STAGE = K::kStage, HALF = K::kHalf;
+  constexpr int VM = (NST - 1) * 2 * LOADS;  // loads younger than a stage when it is read
+  static_assert(VM <= 63, "vmcnt range");
+  __shared__ __align__(1024) char s_ring[NST * STAGE];
+
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int g = lane % 16;   // query row (column of the products)
+  const int jq = lane / 16;  // token quarter: tokens 4 jq .. 4 jq + 3 of a tile
+
+  Work<TK> wk;
+  wk.init(a, w, lane);
+  const int n_my = wk.n_my;
+  if (n_my == 0) return;
+  const int A = wk.A, A_end = A + n_my;
+  Cursor cc = wk.locate(lane);
+
+  // ---- per-lane LDS addresses (within a stage) of the operands, and of the loads
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
+  uint32_t ka[KB], va[NB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {  // lane (g = token, jq) takes chunk jq * KB + kb of row g
+    const int c = jq * KB + kb;
+    ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz(g)) * 16));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {  // lane 16 jq + 4 i + q: row 4 jq + i, dims 16 nb + 4 q
+    const int r = 4 * jq + (g >> 2), q = g & 3;
+    const int c = 2 * nb + (q >> 1);
+    va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz(r)) * 16) + (q & 1) * 8);
+  }
+  // load i, lane l fills LDS position 64 i + l of a half: row r, chunk position p, which
+  // holds chunk p ^ swz(r) of the row; lo[i] is its byte offset from the row slot start
+  const int bsz = a.block_size;
+  uint32_t lo[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = i * 64 + lane;
+    const int r = pos / NC, p = pos % NC;
+    const int rr = bsz >= TK ? r : (r & (bsz - 1));  // row within its block
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((p ^ swz(r)) * 16));
+  }
+
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+  const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
+  const uint64_t block_bytes = head_bytes * static_cast<uint64_t>(a.num_kv_heads);
+  // Issue the loads of tile f into stage st.  A tile spans one block for block sizes 16
+  // and 32 and two for block size 8 (rows 0-7 and 8-15).  Phantom tiles past the share
+  // read block 0, and so do row slots past the context: valid addresses, data unused.
+  auto fetch = [&](const Cursor& f, bool real, int st) __attribute__((always_inline)) -> bool {
+    bool bad = false;
+    const int kvh = real ? f.unit / a.n_gtiles : 0;
+    const int tok0 = f.t * TK;
+    const int32_t* trow = a.block_tables + static_cast<int64_t>(real ? f.s : 0) * a.max_blocks_per_seq;
+    int p0 = 0, p1 = 0;
+    if (real) {
+      p0 = scalar_load(trow + (tok0 >> a.log2_block));
+      if (p0 < 0 || p0 >= a.num_blocks) {
+        bad = true;
+        p0 = 0;
+      }
+      if (bsz < TK && tok0 + bsz < f.ctx) {
+        p1 = scalar_load(trow + (tok0 >> a.log2_block) + 1);
+        if (p1 < 0 || p1 >= a.num_blocks) {
+          bad = true;
+          p1 = 0;
+        }
+      }
+    }
+    const uint64_t head = static_cast<uint64_t>(kvh) * head_bytes;
+    const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
+                        static_cast<uint64_t>(tok0 & (bsz - 1)) * ROW;
+    const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
+    char* stage = s_ring + st * STAGE;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bool second = bsz < TK && i * K::kRowsPerLoad >= 8;  // wave-uniform
+      const uint64_t off = (second ? b1 : b0) + lo[i];
+      __builtin_amdgcn_global_load_lds(kcache + off, stage + i * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vcache + off, stage + HALF + i * 1024, 16, 0, 0);
+    }
+    return bad;
+  };
+
+  // ---- per-piece state
+  f16x8 qop[KB];   // B operand of the scores: lane (g, jq) holds q[g][8 (jq KB + kb) ..]
+  f32x4 o[NB];     // lane (g, jq): O[g][16 nb + 4 jq + i]
+  float m = -INFINITY, l = 0.0f;  // row g: reference (log2 units) and this lane's exp-sum
+  int h0 = 0, ng = 0;
+  bool piece_bad = false;
+  const f16* qp = static_cast<const f16*>(a.q);
+
+  auto piece_start = [&]() __attribute__((always_inline)) {
+    const int kvh = cc.unit / a.n_gtiles;
+    const int gtile = cc.unit - kvh * a.n_gtiles;
+    h0 = kvh * a.group + gtile * kMfRows;
+    ng = min(kMfRows, a.group - gtile * kMfRows);
+    const f16* qrow = qp + (static_cast<int64_t>(cc.s) * a.num_q_heads + h0 + min(g, ng - 1)) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const u32x4 x = load16(qrow + (jq * KB + kb) * 8);
+      qop[kb] = g < ng ? __builtin_bit_cast(f16x8, x) : f16x8{};
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m = -INFINITY;
+    l = 0.0f;
+    piece_bad = false;
+    if (cc.t == 0 && lane == 0)
+      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q is in, once per piece (see above)
+  };
+
+  auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
+    constexpr float kRebase = 8.0f;
+    // scores: two accumulation chains halve the dependent-product latency
+    f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (kb & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[kb], sb, 0, 0, 0);
+      else sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[kb], sa, 0, 0, 0);
+    }
+    const f32x4 sc = sa + sb;
+    const bool full = cn >= TK;  // wave-uniform
+    bool ok[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ok[i] = full || (4 * jq + i < cn);
+      mt = fmaxf(mt, ok[i] ? sc[i] : -INFINITY);
+    }
+    {  // the row maximum over the tile: lanes g, g+16, g+32, g+48
+      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
+      mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
+      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
+      mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
+    }
+    mt *= a.scale_log2;  // scale > 0
+    if (__builtin_amdgcn_ballot_w64(mt > m + kRebase) != 0) {
+      const float m_new = fmaxf(m, mt);
+      const float corr = rescale(m, m_new);
+      l *= corr;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb] *= corr;
+      m = m_new;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -m)) : 0.0f;
+      l += p[i];
+    }
+    const f16x4 pb = {static_cast<f16>(p[0]), static_cast<f16>(p[1]), static_cast<f16>(p[2]),
+                      static_cast<f16>(p[3])};
+    if (!full) {  // V rows past the context (poison or block 0) must not reach O
+      const uint32_t mlo = (ok[0] ? 0x0000FFFFu : 0u) | (ok[1] ? 0xFFFF0000u : 0u);
+      const uint32_t mhi = (ok[2] ? 0x0000FFFFu : 0u) | (ok[3] ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint64_t x = __builtin_bit_cast(uint64_t, vop[nb]);
+        x &= (static_cast<uint64_t>(mhi) << 32) | mlo;
+        vop[nb] = __builtin_bit_cast(f16x4, x);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop[nb], pb, o[nb], 0, 0, 0);
+  };
+
+  // finish the piece that ends with the current tile: the row's exp-sum over its four
+  // lanes, then the rows (whole segment) or a piece record (segment shared with others)
+  auto piece_end = [&]() __attribute__((always_inline)) {
+    float lt = l;
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(lt), as_u(lt), false, false);
+      lt = as_f(x32[0]) + as_f(x32[1]);
+      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(lt), as_u(lt), false, false);
+      lt = as_f(x16[0]) + as_f(x16[1]);
+    }
+    if (g >= ng) return;
+    const bool whole = cc.gstart >= A && cc.gstart + cc.nt <= A_end;
+    const bool head = cc.gstart < A;
+    const float qnan = __builtin_nanf("");
+    const float inv = piece_bad ? qnan : 1.0f / lt;
+    const int64_t row = static_cast<int64_t>(cc.s) * a.num_q_heads + h0 + g;
+    const int rec = w * 2 + (head ? 0 : 1);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = 16 * nb + 4 * jq;
+      const f32x4 y = o[nb] * inv;
+      if (whole) {
+        const f16x4 h = {static_cast<f16>(y[0]), static_cast<f16>(y[1]), static_cast<f16>(y[2]),
+                         static_cast<f16>(y[3])};
+        *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + row * D + col) = h;
+      } else {
+        *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * kMfRows + g) * D + col) = y;
+      }
+    }
+    if (!whole && jq == 0) {
+      a.rec_m[rec * kMfRows + g] = piece_bad ? qnan : m;
+      a.rec_l[rec * kMfRows + g] = piece_bad ? qnan : lt;
+    }
+  };
+
+  f16x8 kop[KB];
+  f16x4 vop[NB];
+  bool fbad[NST];
+  auto process = [&](int i, int st) __attribute__((always_inline)) {
+    if (i == 0 || cc.t == 0) piece_start();
+    piece_bad |= fbad[st];
+    consume(min(TK, cc.ctx - cc.t * TK), kop, vop);
+    if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
+    wk.advance(cc);
+  };
+
+  // ---- main loop, unrolled by the ring depth so that stage offsets are immediates: the
+  // fetch cursor runs NST - 1 tiles ahead; every step issues the same loads
+  Cursor cf = cc;
+  unroll<NST - 1>([&](auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    fbad[st] = fetch(cf, st < n_my, st);
+    wk.advance(cf);
+  });
+  for (int i0 = 0; i0 < n_my; i0 += NST) {
+    unroll<NST>([&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int nxt = (st + NST - 1) % NST;  // the stage the previous tile was read from
+      const int i = i0 + st;
+      fbad[nxt] = fetch(cf, i + NST - 1 < n_my, nxt);
+      wk.advance(cf);
+      read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop);
+      if (i < n_my) process(i, st);
+    });
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS at exit
+}
+
+// ---------------------------------------------------------------------------
 // decode, pass 2: one wave per (sequence, query head).  Empty or invalid contexts get
 // their zero or NaN row here; a segment held whole by one wave was written by it; a
 // segment split over waves w0..w1 is merged from the tail record of w0 and the head
@@ -743,7 +1161,10 @@ int check_common(int dtype, int head_dim, int block_size) {
   return PA_OK;
 }
 
-int group_tile(int group) {  // query heads per wave: 1, 2, 4 or 8 (padded rows are masked)
+// Query rows per wave: the fp16 kernel's products take 16 (unused ones are zero); the
+// fp32 kernel keeps 1, 2, 4 or 8 rows in registers (padded rows are masked).
+int group_tile(int group, int dtype) {
+  if (dtype == PA_F16) return kMfRows;
   return group >= 5 ? 8 : group >= 3 ? 4 : group;
 }
 
@@ -764,10 +1185,10 @@ int64_t waves_for_partition(int64_t num_seqs, int n_units, int max_context_len, 
 }
 
 Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
-              int max_context_len, int partition_size) {
+              int max_context_len, int partition_size, int dtype) {
   Geom g;
   const int group = num_q_heads / num_kv_heads;
-  g.gt = group_tile(group);
+  g.gt = group_tile(group, dtype);
   g.n_gtiles = (group + g.gt - 1) / g.gt;
   g.n_units = num_kv_heads * g.n_gtiles;
   int64_t w = kMaxWaves;
@@ -801,6 +1222,8 @@ struct DecodeCall {
 int check_decode(const DecodeCall& c, Geom* g) {
   int rc = check_common(c.dtype, c.head_dim, c.block_size);
   if (rc != PA_OK) return rc;
+  if (!(c.scale > 0.0f) || !std::isfinite(c.scale))
+    return fail(PA_ERR_INVALID_ARG, "scale %g must be positive and finite", static_cast<double>(c.scale));
   if (c.num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs %d < 0", c.num_seqs);
   if (c.num_kv_heads <= 0 || c.num_q_heads <= 0)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d and num_kv_heads %d must be > 0", c.num_q_heads, c.num_kv_heads);
@@ -816,7 +1239,8 @@ int check_decode(const DecodeCall& c, Geom* g) {
     return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of block_size %d",
                 c.partition_size, c.block_size);
   if (c.num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", c.num_seqs);
-  *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size);
+  *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size,
+                c.dtype);
   // tile counts are 32-bit in the kernel (a tile holds at least 8 tokens)
   if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8) >
       (static_cast<int64_t>(1) << 31) - 1)
@@ -857,45 +1281,70 @@ WsParts split_workspace(void* ws, const Geom& g) {
   return p;
 }
 
-// Resident one-wave work-groups of a kernel on the current device (cached per device
-// and kernel; the answer is fixed for a given build and device).
-template <typename T, int D, int GT>
-int resident_waves() {
+// Resident one-wave work-groups of a kernel on the current device, and the device's
+// compute units (cached per device and kernel: fixed for a given build and device).
+struct Residency {
+  int waves = 0, cus = 0;
+};
+
+Residency residency(const void* kernel) {
   static std::mutex mu;
-  static int cache[64] = {0};
+  static const void* keys[64][8] = {};
+  static Residency vals[64][8];
   int dev = 0;
+  Residency r;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
     (void)hipGetLastError();
-    return kMaxWaves;
+    return r;
   }
   std::lock_guard<std::mutex> lock(mu);
-  if (cache[dev] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, pa_stream_kernel<T, D, GT>, kWave, 0) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        per_cu <= 0 || cus <= 0) {
-      (void)hipGetLastError();
-      return kMaxWaves;
+  for (int i = 0; i < 8; ++i) {
+    if (keys[dev][i] == kernel) return vals[dev][i];
+    if (keys[dev][i] == nullptr) {
+      int per_cu = 0, cus = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess ||
+          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          per_cu <= 0 || cus <= 0) {
+        (void)hipGetLastError();
+        return r;
+      }
+      r.waves = per_cu * cus;
+      r.cus = cus;
+      keys[dev][i] = kernel;
+      vals[dev][i] = r;
+      return r;
     }
-    cache[dev] = per_cu * cus;
   }
-  return cache[dev];
+  return r;
 }
 
-// Waves of one launch: the resident count (at most kMaxWaves), raised with
-// partition_size > 0; never more than the workspace has records for.
-template <typename T, int D, int GT>
-int waves_for(const DecodeCall& c, const Geom& g) {
-  int64_t w = resident_waves<T, D, GT>();
-  if (w > kMaxWaves) w = kMaxWaves;
+// Waves of one launch: `base` (the default split), raised with partition_size > 0;
+// never more than the workspace has records for.
+int waves_for(const DecodeCall& c, const Geom& g, int64_t base) {
+  int64_t w = base > 0 ? base : kMaxWaves;
   const int64_t want = waves_for_partition(c.num_seqs, g.n_units, c.max_context_len, c.partition_size);
   if (want > w) w = want;
   if (w > g.w_cap) w = g.w_cap;
   return static_cast<int>(w < 1 ? 1 : w);
 }
 
+// fp32: every resident wave (at most kMaxWaves).  fp16: kMfWavesPerCU per compute unit:
+// a few deep streams per unit keep HBM busy with less contention than a full unit.
 template <typename T, int D, int GT>
-int launch_stream(const DecodeCall& c, const Geom& g) {
+int waves_valu(const DecodeCall& c, const Geom& g) {
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_kernel<T, D, GT>));
+  return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
+}
+
+template <int D>
+int waves_mfma(const DecodeCall& c, const Geom& g) {
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, kMfStages>));
+  int64_t base = static_cast<int64_t>(r.cus) * kMfWavesPerCU;
+  if (base > r.waves) base = r.waves;
+  return waves_for(c, g, base);
+}
+
+StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   const WsParts ws = split_workspace(c.workspace, g);
   StreamArgs a;
   a.out = c.out;
@@ -920,9 +1369,24 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
   a.max_blocks_per_seq = c.max_blocks_per_seq;
   a.max_context_len = c.max_context_len;
   a.num_blocks = c.num_blocks;
-  a.num_waves = waves_for<T, D, GT>(c, g);
+  a.num_waves = 1;
+  return a;
+}
+
+template <typename T, int D, int GT>
+int launch_stream(const DecodeCall& c, const Geom& g) {
+  StreamArgs a = stream_args(c, g);
+  a.num_waves = waves_valu<T, D, GT>(c, g);
   hipLaunchKernelGGL((pa_stream_kernel<T, D, GT>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_kernel launch");
+}
+
+template <int D>
+int launch_stream_mfma(const DecodeCall& c, const Geom& g) {
+  StreamArgs a = stream_args(c, g);
+  a.num_waves = waves_mfma<D>(c, g);
+  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, kMfStages>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  return check_hip("pa_stream_mfma_kernel launch");
 }
 
 template <typename T, int D, int GT>
@@ -935,14 +1399,19 @@ int launch_reduce(const DecodeCall& c, const Geom& g) {
   return check_hip("pa_reduce_kernel launch");
 }
 
-template <int Which, typename T, int D>
-int dispatch_gt(const DecodeCall& c, const Geom& g) {
+template <int Which, int D>
+int dispatch_f32(const DecodeCall& c, const Geom& g) {
   switch (g.gt) {
-    case 1: return Which == 0 ? launch_stream<T, D, 1>(c, g) : launch_reduce<T, D, 1>(c, g);
-    case 2: return Which == 0 ? launch_stream<T, D, 2>(c, g) : launch_reduce<T, D, 2>(c, g);
-    case 4: return Which == 0 ? launch_stream<T, D, 4>(c, g) : launch_reduce<T, D, 4>(c, g);
-    default: return Which == 0 ? launch_stream<T, D, 8>(c, g) : launch_reduce<T, D, 8>(c, g);
+    case 1: return Which == 0 ? launch_stream<float, D, 1>(c, g) : launch_reduce<float, D, 1>(c, g);
+    case 2: return Which == 0 ? launch_stream<float, D, 2>(c, g) : launch_reduce<float, D, 2>(c, g);
+    case 4: return Which == 0 ? launch_stream<float, D, 4>(c, g) : launch_reduce<float, D, 4>(c, g);
+    default: return Which == 0 ? launch_stream<float, D, 8>(c, g) : launch_reduce<float, D, 8>(c, g);
   }
+}
+
+template <int Which, int D>
+int dispatch_f16(const DecodeCall& c, const Geom& g) {
+  return Which == 0 ? launch_stream_mfma<D>(c, g) : launch_reduce<f16, D, kMfRows>(c, g);
 }
 
 // Which = 0: the stream kernel; 1: the reduce kernel
@@ -950,8 +1419,8 @@ template <int Which>
 int dispatch(const DecodeCall& c, const Geom& g) {
   if (c.num_seqs == 0) return PA_OK;
   if (c.dtype == PA_F16)
-    return c.head_dim == 64 ? dispatch_gt<Which, f16, 64>(c, g) : dispatch_gt<Which, f16, 128>(c, g);
-  return c.head_dim == 64 ? dispatch_gt<Which, float, 64>(c, g) : dispatch_gt<Which, float, 128>(c, g);
+    return c.head_dim == 64 ? dispatch_f16<Which, 64>(c, g) : dispatch_f16<Which, 128>(c, g);
+  return c.head_dim == 64 ? dispatch_f32<Which, 64>(c, g) : dispatch_f32<Which, 128>(c, g);
 }
 
 template <typename T, int D>
@@ -1037,7 +1506,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
       max_context_len < 0 || partition_size < 0 || num_q_heads % num_kv_heads != 0)
     return 0;
-  return geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size).ws_bytes;
+  // the larger of the two layouts, so one workspace serves either element type
+  const size_t a = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size,
+                            PA_F32).ws_bytes;
+  const size_t b = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size,
+                            PA_F16).ws_bytes;
+  return a > b ? a : b;
 }
 
 int pa_decode_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -1070,7 +1544,7 @@ int pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
   if (num_seqs == 0) return PA_OK;
-  const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, dtype);
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(out, 16) || !aligned(context_lens, 4)) return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);
