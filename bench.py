@@ -24,7 +24,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "paged_kv_cache_167_amd", "csrc", "pa_kernels.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pa_stream_kernel_llama3_8b_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def stream_kernel_name(is_f16):
+    """The first-pass kernel that pa_decode launches for this element type."""
+    return "pa_stream_mfma_kernel" if is_f16 else "pa_stream_kernel"
+
+
+def traffic_file(kernel, config):
+    return os.path.join(PROFILES, f"{kernel}_{config}_traffic.json")
 
 
 def log(msg):
@@ -63,12 +72,13 @@ def kernel_sha():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(config, partition):
+def measured_traffic(kernel, config, partition):
     """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs, if they were taken
     on the current kernel source and the same workload; otherwise None."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(kernel, config)
+    if not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         t = json.load(f)
     if t.get("kernel_source_sha256") != kernel_sha() or t.get("config") != config or \
             t.get("partition") != partition:
@@ -87,19 +97,22 @@ def cpu_baseline(case):
     n = case.num_seqs
     if case.kv_bytes() > 1.5e9:  # keep the CPU leg to tens of seconds: a prefix of the batch
         n = max(1, int(n * 1.5e9 / case.kv_bytes()))
+    reps = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc, vc,
-                                 case.block_size)
-        O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n], case.scale,
-                 case.block_size, case.num_kv_heads)
-        dt = time.perf_counter() - t0
+        while reps == 0 or time.perf_counter() - t0 < 10.0:  # about 10 s of CPU work
+            kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc, vc,
+                                     case.block_size)
+            O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n],
+                     case.scale, case.block_size, case.num_kv_heads)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
     kv = int(case.context_lens[:n].astype("int64").sum()) * case.num_kv_heads * case.head_dim * \
         2 * case.elt_bytes
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds": dt, "seqs_per_s": n / dt,
-            "sample": f"{n} of {case.num_seqs} sequences, one step (write new tokens + decode), "
-                      "numpy float64, BLAS limited to 1 thread"}
+            "seconds_per_step": dt, "steps": reps, "seqs_per_s": n / dt,
+            "sample": f"{n} of {case.num_seqs} sequences, {reps} steps (write new tokens + "
+                      "decode) of about 10 s in total, numpy float64, BLAS limited to 1 thread"}
 
 
 def main():
@@ -176,12 +189,14 @@ def main():
     kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     kern_ms_avg = float(np.mean(kern_ms))
 
-    # cold-cache launches of the same kernel: a 1 GiB write evicts L2 and the 256 MB MALL
+    # cold-cache launches of the same kernel: reading 1 GiB first leaves L2 and the 256 MB
+    # MALL holding clean lines of other data (a write would leave dirty lines whose
+    # write-back then competes with the kernel's reads)
     cold_ms = []
     if args.cold_iters > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_iters):
-            flush.fill_(1.0)
+            flush.sum()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             step(e0, e1)
             torch.cuda.synchronize()
@@ -195,7 +210,8 @@ def main():
     alg_bytes = kv_bytes + 2 * q_bytes + tokens_blocks * 4 + case.num_seqs * 4
     achieved = alg_bytes / (kern_ms_avg * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic = measured_traffic(args.config, partition)
+    kernel = stream_kernel_name(case.dtype == np.float16)
+    traffic = measured_traffic(kernel, args.config, partition)
 
     result = {
         "metric": "paged decode KV GB/s and % of MI355X HBM peak; sequences/s per layer",
@@ -222,7 +238,7 @@ def main():
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "roofline": {
-            "kernel": "pa_stream_kernel",
+            "kernel": kernel,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
