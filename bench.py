@@ -160,45 +160,56 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step(ev0=None, ev1=None):
+    def step():
         P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
-        if ev0 is not None:
-            ev0.record(stream)
+        P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
+                    case.num_kv_heads, max_context_len=mcl, partition_size=partition,
+                    workspace=ws, stream=stream)
+
+    def stream_kernel():  # the first of pa_decode's two launches, on its own
         P.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale,
                                case.block_size, case.num_kv_heads, max_context_len=mcl,
                                partition_size=partition, workspace=ws, stream=stream)
-        if ev1 is not None:
-            ev1.record(stream)
-        P.pa_decode_reduce(out, ctx, case.num_kv_heads, mcl, partition, ws, stream=stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # the timed steps: nothing but the path's own launches between the two synchronisations
+    # (an event recorded between two kernels costs several microseconds of GPU time)
     log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
-    kern_ms_avg = float(np.mean(kern_ms))
+
+    # the dominant kernel alone: the same number of back-to-back launches between two HIP
+    # events on the launch stream; their average is its launch duration
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream_kernel()
+    e0.record(stream)
+    for _ in range(args.steps):
+        stream_kernel()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms_avg = e0.elapsed_time(e1) / args.steps
+    step()  # leave the rows pa_decode writes in out
+    torch.cuda.synchronize()
 
     # cold-cache launches of the same kernel: reading 1 GiB first leaves L2 and the 256 MB
     # MALL holding clean lines of other data (a write would leave dirty lines whose
-    # write-back then competes with the kernel's reads)
+    # write-back then competes with the kernel's reads); one launch between two events
     cold_ms = []
     if args.cold_iters > 0:
         flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         for _ in range(args.cold_iters):
             flush.sum()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            step(e0, e1)
+            e0.record(stream)
+            stream_kernel()
+            e1.record(stream)
             torch.cuda.synchronize()
             cold_ms.append(e0.elapsed_time(e1))
         del flush

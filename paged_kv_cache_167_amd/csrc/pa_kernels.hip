@@ -310,10 +310,10 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(
 // it has ceil(ctx / TK) tiles.  Segments are ordered by sequence, then unit.
 struct StreamArgs {
   void* out;
-  int2* seg_desc;  // [S * n_units] {first wave, last wave} holding pieces of the segment
-  float* rec_m;    // [2 * W * GT] per piece record: running max (log2 units) per row
-  float* rec_l;    // [2 * W * GT] exp-sum per row
-  float* rec_o;    // [2 * W * GT * D] normalised output per row
+  int2* seg_desc;       // [S * n_units] {first wave, last wave} holding pieces of the segment
+  float* rec_m;         // [2 * W * rec_rows] per piece record: running max (log2 units) per row
+  float* rec_l;         // [2 * W * rec_rows] exp-sum per row
+  float* rec_o;         // [2 * W * rec_rows * D] normalised output per row
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -332,6 +332,7 @@ struct StreamArgs {
   int max_context_len;
   int64_t num_blocks;
   int num_waves;
+  int rec_rows;  // query rows per piece record
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -414,6 +415,50 @@ struct Work {
     } while (c.nt == 0 && c.s < S);
   }
 };
+
+// ---------------------------------------------------------------------------
+// merging the pieces of a split context (log-sum-exp over pieces, in token order)
+// ---------------------------------------------------------------------------
+
+// One wave merges query row g of a segment whose pieces are the records of waves
+// first .. first + npieces - 1: the tail record of the first, then the head records of
+// the others.  Piece p has running max m_p (log2 units), exp-sum l_p and normalised
+// output o_p; with M = max m_p, out = sum_p w_p o_p / sum_p w_p, w_p = l_p 2^(m_p - M),
+// accumulated in piece order.  Lane p holds piece p's (m, l); the weights are broadcast
+// with readlane and each lane sums the outputs of its dims.
+template <typename T, int D>
+__device__ __forceinline__ void merge_row(T* dst, const float* rec_m, const float* rec_l,
+                                          const float* rec_o, int first, int npieces, int rec_rows,
+                                          int g, int lane) {
+  constexpr int kDPL = D / kWave;  // dims per lane
+  auto rec_of = [&](int p) { return p == 0 ? first * 2 + 1 : (first + p) * 2; };
+  float big_m = -INFINITY, den = 0.0f;
+  float num[kDPL];
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) num[k] = 0.0f;
+  for (int p0 = 0; p0 < npieces; p0 += kWave) {
+    const int p = p0 + lane;
+    const int r = p < npieces ? rec_of(p) * rec_rows + g : 0;
+    const float mp = p < npieces ? rec_m[r] : -INFINITY;
+    const float lp = p < npieces ? rec_l[r] : 0.0f;
+    const float m_new = fmaxf(big_m, wave_max(mp));
+    const float c_old = rescale(big_m, m_new);
+    const float wp = p < npieces ? lp * __builtin_amdgcn_exp2f(mp - m_new) : 0.0f;
+    den = den * c_old + wave_sum(wp);
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) num[k] *= c_old;
+    const int cnt = min(kWave, npieces - p0);
+    for (int i = 0; i < cnt; ++i) {
+      const float wgt = as_f(__builtin_amdgcn_readlane(as_u(wp), i));
+      const float* o = rec_o + (static_cast<int64_t>(rec_of(p0 + i)) * rec_rows + g) * D;
+#pragma unroll
+      for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, o[k * kWave + lane], num[k]);
+    }
+    big_m = m_new;
+  }
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(num[k] / den);
+}
 
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
@@ -655,15 +700,15 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
         if (whole) {
           *reinterpret_cast<u32x4*>(static_cast<T*>(a.out) + (row0 + g) * D + col) = pack16<T>(o);
         } else {
-          float* dst = a.rec_o + (static_cast<int64_t>(rec) * GT + g) * D + col;
+          float* dst = a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + g) * D + col;
 #pragma unroll
           for (int e = 0; e < E; e += 4)
             *reinterpret_cast<u32x4*>(dst + e) = pack16<float>(&o[e]);
         }
       }
       if (!whole && sub == 0) {
-        a.rec_m[rec * GT + g] = piece_bad ? qnan : m[g];
-        a.rec_l[rec * GT + g] = piece_bad ? qnan : l[g];
+        a.rec_m[rec * a.rec_rows + g] = piece_bad ? qnan : m[g];
+        a.rec_l[rec * a.rec_rows + g] = piece_bad ? qnan : l[g];
       }
     }
   };
@@ -731,7 +776,8 @@ struct MCfg {
   static constexpr int kLoads = kHalf / 1024;  // 1 KB direct-to-LDS loads for each of K and V
   static constexpr int kKB = D / 32;           // products for the scores
   static constexpr int kNB = D / 16;           // products for P.V
-  static constexpr int kStage = 2 * kHalf;     // one ring stage: the K tile, then the V tile
+  static constexpr int kQ = kMfRows * kRow;      // q rows of a piece (at most 16)
+  static constexpr int kStage = 2 * kHalf + kQ;  // one ring stage: K tile, V tile, q rows
   static constexpr int kRowsPerLoad = 64 / kNC;
   static_assert(kLoads * kRowsPerLoad == kTK, "a load covers whole rows");
 };
@@ -743,59 +789,109 @@ struct MCfg {
 // x 2 chunks) do too.
 __device__ __forceinline__ int swz(int r) { return (2 * r + (r >> 2)) & 7; }
 
-// Read one ring stage's operands: wait until at most VM vector-memory operations are
-// outstanding (the stage's own loads are older), then the K operands (ds_read_b128) and
-// the V^T operands (ds_read_b64_tr_b16) at the lane's addresses + OFF, then wait for the
-// reads.  One asm block, so the compiler's conservative tracking of direct-to-LDS loads
-// cannot put a full drain in front of the reads.
+// A wave-uniform pointer, forced into SGPRs (an asm "s" operand needs it there).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t a = reinterpret_cast<uintptr_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  return reinterpret_cast<const T*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Read one ring stage's operands, and load the two block-table entries the next fetch
+// needs.  In order: issue the two scalar loads of the entries; wait until at most VM
+// vector-memory operations are outstanding (the stage's own loads are older); read the K
+// operands (ds_read_b128) and the V^T operands (ds_read_b64_tr_b16) at the lane's
+// addresses + OFF; wait for the reads and the entries (lgkmcnt counts both).  The entry
+// loads thus overlap the wait for the stage instead of stalling the fetch.  One asm block,
+// so the compiler's conservative tracking of direct-to-LDS loads cannot put a full drain
+// in front of the reads.  Outputs are early-clobber: the reads complete asynchronously,
+// so no output may share a register with an address still to be read.
 template <int VM, int OFF>
 __device__ __forceinline__ void read_stage_d128(const uint32_t (&ka)[4], const uint32_t (&va)[8],
-                                                f16x8 (&k)[4], f16x4 (&v)[8]) {
+                                                f16x8 (&k)[4], f16x4 (&v)[8], const int32_t* e0,
+                                                const int32_t* e1, int32_t& p0, int32_t& p1) {
   asm volatile(
+      "s_load_dword %[p0], %[e0], 0x0\n\t"
+      "s_load_dword %[p1], %[e1], 0x0\n\t"
       "s_waitcnt vmcnt(%[vm])\n\t"
-      "ds_read_b128 %0, %12 offset:%[off]\n\t"
-      "ds_read_b128 %1, %13 offset:%[off]\n\t"
-      "ds_read_b128 %2, %14 offset:%[off]\n\t"
-      "ds_read_b128 %3, %15 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %4, %16 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %5, %17 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %6, %18 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %7, %19 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %8, %20 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %9, %21 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %10, %22 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %11, %23 offset:%[off]\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b128 %[k1], %[ka1] offset:%[off]\n\t"
+      "ds_read_b128 %[k2], %[ka2] offset:%[off]\n\t"
+      "ds_read_b128 %[k3], %[ka3] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v3], %[va3] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v4], %[va4] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v5], %[va5] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v6], %[va6] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v7], %[va7] offset:%[off]\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(k[0]), "=v"(k[1]), "=v"(k[2]), "=v"(k[3]), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]),
-        "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]), "=v"(v[7])
-      : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(va[0]), "v"(va[1]), "v"(va[2]),
-        "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]), [vm] "n"(VM), [off] "n"(OFF)
+      : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [k2] "=&v"(k[2]), [k3] "=&v"(k[3]), [v0] "=&v"(v[0]),
+        [v1] "=&v"(v[1]), [v2] "=&v"(v[2]), [v3] "=&v"(v[3]), [v4] "=&v"(v[4]), [v5] "=&v"(v[5]),
+        [v6] "=&v"(v[6]), [v7] "=&v"(v[7]), [p0] "=&s"(p0), [p1] "=&s"(p1)
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [va0] "v"(va[0]),
+        [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]), [va5] "v"(va[5]),
+        [va6] "v"(va[6]), [va7] "v"(va[7]), [e0] "s"(e0), [e1] "s"(e1), [vm] "n"(VM), [off] "n"(OFF)
       : "memory");
 }
 
 template <int VM, int OFF>
 __device__ __forceinline__ void read_stage_d64(const uint32_t (&ka)[2], const uint32_t (&va)[4],
-                                               f16x8 (&k)[2], f16x4 (&v)[4]) {
+                                               f16x8 (&k)[2], f16x4 (&v)[4], const int32_t* e0,
+                                               const int32_t* e1, int32_t& p0, int32_t& p1) {
   asm volatile(
+      "s_load_dword %[p0], %[e0], 0x0\n\t"
+      "s_load_dword %[p1], %[e1], 0x0\n\t"
       "s_waitcnt vmcnt(%[vm])\n\t"
-      "ds_read_b128 %0, %6 offset:%[off]\n\t"
-      "ds_read_b128 %1, %7 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%[off]\n\t"
-      "ds_read_b64_tr_b16 %5, %11 offset:%[off]\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b128 %[k1], %[ka1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v3], %[va3] offset:%[off]\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=v"(k[0]), "=v"(k[1]), "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3])
-      : "v"(ka[0]), "v"(ka[1]), "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), [vm] "n"(VM),
-        [off] "n"(OFF)
+      : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]),
+        [v3] "=&v"(v[3]), [p0] "=&s"(p0), [p1] "=&s"(p1)
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]),
+        [va3] "v"(va[3]), [e0] "s"(e0), [e1] "s"(e1), [vm] "n"(VM), [off] "n"(OFF)
       : "memory");
 }
 
 template <int D, int VM, int OFF>
 __device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], const uint32_t (&va)[D / 16],
-                                              f16x8 (&k)[D / 32], f16x4 (&v)[D / 16]) {
-  if constexpr (D == 128) read_stage_d128<VM, OFF>(ka, va, k, v);
-  else read_stage_d64<VM, OFF>(ka, va, k, v);
+                                              f16x8 (&k)[D / 32], f16x4 (&v)[D / 16], const int32_t* e0,
+                                              const int32_t* e1, int32_t& p0, int32_t& p1) {
+  if constexpr (D == 128) read_stage_d128<VM, OFF>(ka, va, k, v, e0, e1, p0, p1);
+  else read_stage_d64<VM, OFF>(ka, va, k, v, e0, e1, p0, p1);
+}
+
+// Read a piece's q operand from LDS: chunks kb = 0 .. KB-1 at the lane's address + OFF +
+// 16 kb.  Called after the stage wait that covers the q loads; asm for the same reason
+// as the stage reads.
+template <int KB, int OFF>
+__device__ __forceinline__ void read_q_mf(uint32_t addr, f16x8 (&q)[KB]) {
+  if constexpr (KB == 4) {
+    asm volatile(
+        "ds_read_b128 %[q0], %[a] offset:%[o0]\n\t"
+        "ds_read_b128 %[q1], %[a] offset:%[o1]\n\t"
+        "ds_read_b128 %[q2], %[a] offset:%[o2]\n\t"
+        "ds_read_b128 %[q3], %[a] offset:%[o3]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [q0] "=&v"(q[0]), [q1] "=&v"(q[1]), [q2] "=&v"(q[2]), [q3] "=&v"(q[3])
+        : [a] "v"(addr), [o0] "n"(OFF), [o1] "n"(OFF + 16), [o2] "n"(OFF + 32), [o3] "n"(OFF + 48)
+        : "memory");
+  } else {
+    static_assert(KB == 2, "q chunks per lane");
+    asm volatile(
+        "ds_read_b128 %[q0], %[a] offset:%[o0]\n\t"
+        "ds_read_b128 %[q1], %[a] offset:%[o1]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [q0] "=&v"(q[0]), [q1] "=&v"(q[1])
+        : [a] "v"(addr), [o0] "n"(OFF), [o1] "n"(OFF + 16)
+        : "memory");
+  }
 }
 
 // Call f(std::integral_constant<int, i>{}) for i = 0 .. N-1: a loop whose index is a
@@ -814,8 +910,11 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   using K = MCfg<D>;
   constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
   constexpr int LOADS = K::kLoads, STAGE = K::kStage, HALF = K::kHalf;
+  constexpr int QOFF = 2 * HALF;             // q rows within a stage
+  constexpr int QROWS = 1024 / ROW;          // q rows per 1 KB load
   constexpr int VM = (NST - 1) * 2 * LOADS;  // loads younger than a stage when it is read
   static_assert(VM <= 63, "vmcnt range");
+  static_assert(NST * STAGE <= 65536, "stage offsets are 16-bit immediates");
   __shared__ __align__(1024) char s_ring[NST * STAGE];
 
   const int w = blockIdx.x;
@@ -844,6 +943,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const int c = 2 * nb + (q >> 1);
     va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz(r)) * 16) + (q & 1) * 8);
   }
+  // q operand: lane (g, jq) reads chunks jq * KB .. jq * KB + KB - 1 of q row g
+  const uint32_t qa = ring + static_cast<uint32_t>(g * ROW + jq * KB * 16);
   // load i, lane l fills LDS position 64 i + l of a half: row r, chunk position p, which
   // holds chunk p ^ swz(r) of the row; lo[i] is its byte offset from the row slot start
   const int bsz = a.block_size;
@@ -858,28 +959,65 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 
   const char* kcache = static_cast<const char*>(a.k_cache);
   const char* vcache = static_cast<const char*>(a.v_cache);
+  const char* qbytes = static_cast<const char*>(a.q);
   const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
   const uint64_t block_bytes = head_bytes * static_cast<uint64_t>(a.num_kv_heads);
-  // Issue the loads of tile f into stage st.  A tile spans one block for block sizes 16
-  // and 32 and two for block size 8 (rows 0-7 and 8-15).  Phantom tiles past the share
-  // read block 0, and so do row slots past the context: valid addresses, data unused.
-  auto fetch = [&](const Cursor& f, bool real, int st) __attribute__((always_inline)) -> bool {
+
+  // Block-table entries of tile f: the first row slot's, and for block size 8 the second
+  // half's (the first again when that half lies past the context).  A phantom tile past
+  // the share points at entry 0 of row 0, a valid address whose value is not used.
+  auto entry_ptrs = [&](const Cursor& f, bool real, const int32_t*& e0, const int32_t*& e1)
+      __attribute__((always_inline)) {
+    if (!real) {
+      e0 = e1 = uniform_ptr(a.block_tables);
+      return;
+    }
+    const int tok0 = f.t * TK;
+    const int32_t* p = a.block_tables + static_cast<int64_t>(f.s) * a.max_blocks_per_seq +
+                       (tok0 >> a.log2_block);
+    e0 = uniform_ptr(p);
+    e1 = (bsz < TK && tok0 + bsz < f.ctx) ? uniform_ptr(p + 1) : e0;
+  };
+
+  // Issue the loads of tile f into stage st, given its table entries p0, p1: first the q
+  // rows of the piece when the tile starts one (qload), then K and V.  A tile spans one
+  // block for block sizes 16 and 32 and two for block size 8 (rows 0-7 and 8-15).  Phantom
+  // tiles past the share read block 0, and so do row slots past the context: valid
+  // addresses, data unused.  Returns whether an entry lies outside the pool.
+  auto fetch = [&](const Cursor& f, bool real, bool qload, int st, int p0, int p1)
+      __attribute__((always_inline)) -> bool {
     bool bad = false;
     const int kvh = real ? f.unit / a.n_gtiles : 0;
     const int tok0 = f.t * TK;
-    const int32_t* trow = a.block_tables + static_cast<int64_t>(real ? f.s : 0) * a.max_blocks_per_seq;
-    int p0 = 0, p1 = 0;
     if (real) {
-      p0 = scalar_load(trow + (tok0 >> a.log2_block));
       if (p0 < 0 || p0 >= a.num_blocks) {
         bad = true;
         p0 = 0;
       }
       if (bsz < TK && tok0 + bsz < f.ctx) {
-        p1 = scalar_load(trow + (tok0 >> a.log2_block) + 1);
         if (p1 < 0 || p1 >= a.num_blocks) {
           bad = true;
           p1 = 0;
+        }
+      } else {
+        p1 = 0;
+      }
+    } else {
+      p0 = 0;
+      p1 = 0;
+    }
+    char* stage = s_ring + st * STAGE;
+    if (qload) {  // wave-uniform: rows h0 .. h0 + ng - 1 of the piece's sequence
+      const int gtile = f.unit - kvh * a.n_gtiles;
+      const int h0 = kvh * a.group + gtile * kMfRows;
+      const int ng = min(kMfRows, a.group - gtile * kMfRows);
+      const char* qrow0 = qbytes + (static_cast<int64_t>(f.s) * a.num_q_heads + h0) * ROW;
+#pragma unroll
+      for (int i = 0; i < kMfRows / QROWS; ++i) {
+        if (i * QROWS < ng) {
+          const int r = min(i * QROWS + lane / NC, ng - 1);
+          __builtin_amdgcn_global_load_lds(qrow0 + r * ROW + (lane % NC) * 16, stage + QOFF + i * 1024,
+                                           16, 0, 0);
         }
       }
     }
@@ -887,7 +1025,6 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
                         static_cast<uint64_t>(tok0 & (bsz - 1)) * ROW;
     const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
-    char* stage = s_ring + st * STAGE;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       const bool second = bsz < TK && i * K::kRowsPerLoad >= 8;  // wave-uniform
@@ -904,19 +1041,17 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   float m = -INFINITY, l = 0.0f;  // row g: reference (log2 units) and this lane's exp-sum
   int h0 = 0, ng = 0;
   bool piece_bad = false;
-  const f16* qp = static_cast<const f16*>(a.q);
 
-  auto piece_start = [&]() __attribute__((always_inline)) {
+  // Start a piece at the current tile, whose stage stc holds the piece's q rows.
+  auto piece_start = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
     const int kvh = cc.unit / a.n_gtiles;
     const int gtile = cc.unit - kvh * a.n_gtiles;
     h0 = kvh * a.group + gtile * kMfRows;
     ng = min(kMfRows, a.group - gtile * kMfRows);
-    const f16* qrow = qp + (static_cast<int64_t>(cc.s) * a.num_q_heads + h0 + min(g, ng - 1)) * D;
+    read_q_mf<KB, st * STAGE + QOFF>(qa, qop);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const u32x4 x = load16(qrow + (jq * KB + kb) * 8);
-      qop[kb] = g < ng ? __builtin_bit_cast(f16x8, x) : f16x8{};
-    }
+    for (int kb = 0; kb < KB; ++kb) qop[kb] = g < ng ? qop[kb] : f16x8{};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     m = -INFINITY;
@@ -924,7 +1059,6 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     piece_bad = false;
     if (cc.t == 0 && lane == 0)
       a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): q is in, once per piece (see above)
   };
 
   auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
@@ -1008,20 +1142,21 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
                          static_cast<f16>(y[3])};
         *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + row * D + col) = h;
       } else {
-        *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * kMfRows + g) * D + col) = y;
+        *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + g) * D + col) = y;
       }
     }
     if (!whole && jq == 0) {
-      a.rec_m[rec * kMfRows + g] = piece_bad ? qnan : m;
-      a.rec_l[rec * kMfRows + g] = piece_bad ? qnan : lt;
+      a.rec_m[rec * a.rec_rows + g] = piece_bad ? qnan : m;
+      a.rec_l[rec * a.rec_rows + g] = piece_bad ? qnan : lt;
     }
   };
 
   f16x8 kop[KB];
   f16x4 vop[NB];
   bool fbad[NST];
-  auto process = [&](int i, int st) __attribute__((always_inline)) {
-    if (i == 0 || cc.t == 0) piece_start();
+  auto process = [&](int i, auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    if (i == 0 || cc.t == 0) piece_start(stc);
     piece_bad |= fbad[st];
     consume(min(TK, cc.ctx - cc.t * TK), kop, vop);
     if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
@@ -1029,33 +1164,44 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   };
 
   // ---- main loop, unrolled by the ring depth so that stage offsets are immediates: the
-  // fetch cursor runs NST - 1 tiles ahead; every step issues the same loads
+  // fetch cursor runs NST - 1 tiles ahead; every step issues the same K/V loads.  The
+  // table entries of the fetch cursor's tile are always loaded one step ahead.
   Cursor cf = cc;
+  const int32_t *e0, *e1;
+  int32_t pe0, pe1;
+  entry_ptrs(cf, 0 < n_my, e0, e1);
+  pe0 = scalar_load(e0);
+  pe1 = scalar_load(e1);
   unroll<NST - 1>([&](auto stc) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
-    fbad[st] = fetch(cf, st < n_my, st);
+    const bool real = st < n_my;
+    fbad[st] = fetch(cf, real, real && (st == 0 || cf.t == 0), st, pe0, pe1);
     wk.advance(cf);
+    entry_ptrs(cf, st + 1 < n_my, e0, e1);
+    pe0 = scalar_load(e0);
+    pe1 = scalar_load(e1);
   });
   for (int i0 = 0; i0 < n_my; i0 += NST) {
     unroll<NST>([&](auto stc) __attribute__((always_inline)) {
       constexpr int st = decltype(stc)::value;
       constexpr int nxt = (st + NST - 1) % NST;  // the stage the previous tile was read from
       const int i = i0 + st;
-      fbad[nxt] = fetch(cf, i + NST - 1 < n_my, nxt);
+      const bool real = i + NST - 1 < n_my;
+      fbad[nxt] = fetch(cf, real, real && cf.t == 0, nxt, pe0, pe1);
       wk.advance(cf);
-      read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop);
-      if (i < n_my) process(i, st);
+      entry_ptrs(cf, i + NST < n_my, e0, e1);
+      read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      if (i < n_my) process(i, stc);
     });
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS at exit
 }
 
 // ---------------------------------------------------------------------------
-// decode, pass 2: one wave per (sequence, query head).  Empty or invalid contexts get
-// their zero or NaN row here; a segment held whole by one wave was written by it; a
-// segment split over waves w0..w1 is merged from the tail record of w0 and the head
-// records of w0+1..w1, in that order.  Lane p holds piece p's (max, sum); the weights
-// go through LDS and each lane sums the pieces' outputs for its dims.
+// decode, second launch (pa_decode_reduce only; pa_decode merges in its one launch): one
+// wave per (sequence, query head).  Empty or invalid contexts get their zero or NaN row
+// here; a segment held whole by one wave was written by it; a segment split over waves
+// w0..w1 is merged from the tail record of w0 and the head records of w0+1..w1.
 // ---------------------------------------------------------------------------
 
 template <typename T, int D, int GT>
@@ -1063,9 +1209,8 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
     T* __restrict__ out, const int2* __restrict__ seg_desc, const float* __restrict__ rec_m,
     const float* __restrict__ rec_l, const float* __restrict__ rec_o,
     const int32_t* __restrict__ context_lens, int num_q_heads, int group, int n_gtiles,
-    int max_context_len, int w_cap) {
+    int max_context_len, int w_cap, int rec_rows) {
   constexpr int kDPL = D / kWave;  // dims per lane
-  __shared__ float s_w[kWave];
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
@@ -1088,37 +1233,7 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
     for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(__builtin_nanf(""));
     return;
   }
-  const int npieces = d.y - d.x + 1;
-  auto rec_of = [&](int p) { return p == 0 ? d.x * 2 + 1 : (d.x + p) * 2; };
-  float big_m = -INFINITY, den = 0.0f;
-  float num[kDPL];
-#pragma unroll
-  for (int k = 0; k < kDPL; ++k) num[k] = 0.0f;
-  for (int p0 = 0; p0 < npieces; p0 += kWave) {
-    const int p = p0 + lane;
-    const int r = p < npieces ? rec_of(p) * GT + g : 0;
-    const float mp = p < npieces ? rec_m[r] : -INFINITY;
-    const float lp = p < npieces ? rec_l[r] : 0.0f;
-    const float m_new = fmaxf(big_m, wave_max(mp));
-    const float c_old = rescale(big_m, m_new);
-    const float wp = p < npieces ? lp * __builtin_amdgcn_exp2f(mp - m_new) : 0.0f;
-    den = den * c_old + wave_sum(wp);
-#pragma unroll
-    for (int k = 0; k < kDPL; ++k) num[k] *= c_old;
-    __syncthreads();  // the previous group's weights are consumed
-    s_w[lane] = wp;
-    __syncthreads();
-    const int cnt = min(kWave, npieces - p0);
-    for (int i = 0; i < cnt; ++i) {
-      const float wgt = s_w[i];
-      const float* o = rec_o + (static_cast<int64_t>(rec_of(p0 + i)) * GT + g) * D;
-#pragma unroll
-      for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, o[k * kWave + lane], num[k]);
-    }
-    big_m = m_new;
-  }
-#pragma unroll
-  for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(num[k] / den);
+  merge_row<T, D>(dst, rec_m, rec_l, rec_o, d.x, d.y - d.x + 1, rec_rows, g, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -1173,6 +1288,7 @@ struct Geom {
   int gt = 1;        // query heads per unit
   int n_gtiles = 1;  // units per kv head
   int n_units = 1;   // segments per sequence
+  int rec_rows = 1;  // query rows per piece record
   int w_cap = 1;     // waves the workspace has records for
   size_t desc_bytes = 0, rec_ml_bytes = 0, rec_o_bytes = 0, ws_bytes = 0;
 };
@@ -1195,9 +1311,10 @@ Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
   const int64_t want = waves_for_partition(num_seqs, g.n_units, max_context_len, partition_size);
   if (want > w) w = want;
   g.w_cap = static_cast<int>(w > (1 << 28) ? (1 << 28) : w);
+  g.rec_rows = g.gt < group ? g.gt : group;
   g.desc_bytes = align256(static_cast<size_t>(num_seqs) * g.n_units * 2 * sizeof(int));
-  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.gt * sizeof(float));
-  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.gt * head_dim * sizeof(float));
+  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * sizeof(float));
+  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * head_dim * sizeof(float));
   g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
   return g;
 }
@@ -1275,9 +1392,10 @@ WsParts split_workspace(void* ws, const Geom& g) {
   char* b = static_cast<char*>(ws);
   WsParts p;
   p.desc = reinterpret_cast<int2*>(b);
-  p.rec_m = reinterpret_cast<float*>(b + g.desc_bytes);
-  p.rec_l = reinterpret_cast<float*>(b + g.desc_bytes + g.rec_ml_bytes);
-  p.rec_o = reinterpret_cast<float*>(b + g.desc_bytes + 2 * g.rec_ml_bytes);
+  b += g.desc_bytes;
+  p.rec_m = reinterpret_cast<float*>(b);
+  p.rec_l = reinterpret_cast<float*>(b + g.rec_ml_bytes);
+  p.rec_o = reinterpret_cast<float*>(b + 2 * g.rec_ml_bytes);
   return p;
 }
 
@@ -1370,6 +1488,7 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   a.max_context_len = c.max_context_len;
   a.num_blocks = c.num_blocks;
   a.num_waves = 1;
+  a.rec_rows = g.rec_rows;
   return a;
 }
 
@@ -1395,7 +1514,7 @@ int launch_reduce(const DecodeCall& c, const Geom& g) {
   hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
                      c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
                      c.context_lens, c.num_q_heads, c.num_q_heads / c.num_kv_heads, g.n_gtiles,
-                     c.max_context_len, g.w_cap);
+                     c.max_context_len, g.w_cap, g.rec_rows);
   return check_hip("pa_reduce_kernel launch");
 }
 
@@ -1587,3 +1706,4 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
 }
 
 }  // extern "C"
+

@@ -41,26 +41,26 @@ def test_abi_version():
 
 
 def test_workspace_size_query():
-    # per (sequence, unit) a 2-int descriptor; per wave two records of R rows: fp32 max and
-    # sum (each region 256-byte aligned) and R * head_dim fp32 outputs.  fp16 records hold
-    # 16 rows (the matrix-core kernel's query rows) and are the larger layout.
+    # per (sequence, unit) a 2-int descriptor; per wave two records, each with fp32 max and
+    # sum of R rows and R * head_dim fp32 outputs (every region 256-byte aligned).
+    # R = min(rows per unit, group); the larger of the fp32 and fp16 layouts is returned.
     al = lambda x: (x + 255) // 256 * 256
-    R = 16
-    S, hq, hkv, d = 64, 32, 8, 128  # group 4: one unit per kv head
+
+    def layout(S, units, waves, R, d):
+        return al(S * units * 8) + 2 * al(2 * waves * R * 4) + al(2 * waves * R * d * 4)
+
+    S, hq, hkv, d = 64, 32, 8, 128  # group 4: one unit per kv head, 4 rows per record
     waves = 4096
-    want = al(S * hkv * 8) + 2 * al(2 * waves * R * 4) + al(2 * waves * R * d * 4)
-    assert P.pa_decode_workspace_bytes(S, hq, hkv, d, 4096, 0) == want
+    assert P.pa_decode_workspace_bytes(S, hq, hkv, d, 4096, 0) == layout(S, hkv, waves, 4, d)
     # 56 query / 8 kv heads: groups of 7, one unit per kv head
-    want7 = al(8 * 8 * 8) + 2 * al(2 * waves * R * 4) + al(2 * waves * R * d * 4)
-    assert P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 0) == want7
+    assert P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 0) == layout(8, 8, waves, 7, d)
     # a partition size asks for more waves once the batch exceeds 4096 of them
     big = P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 512)
     waves_p = (8 * 8 * 131072 + 511) // 512
-    assert big == al(8 * 8 * 8) + 2 * al(2 * waves_p * R * 4) + al(2 * waves_p * R * d * 4)
-    # 64 query heads per kv head: two units of 16 rows (fp16) or eight of 8 (fp32)
+    assert big == layout(8, 8, waves_p, 7, d)
+    # 64 query heads per kv head: four units of 16 rows (fp16) or eight of 8 (fp32)
     wide = P.pa_decode_workspace_bytes(2, 64, 1, d, 1024, 0)
-    assert wide == max(al(2 * 4 * 8) + 2 * al(2 * waves * 16 * 4) + al(2 * waves * 16 * d * 4),
-                       al(2 * 8 * 8) + 2 * al(2 * waves * 8 * 4) + al(2 * waves * 8 * d * 4))
+    assert wide == max(layout(2, 4, waves, 16, d), layout(2, 8, waves, 8, d))
     assert P.pa_decode_workspace_bytes(0, hq, hkv, d, 4096, 0) == 0
     assert P.pa_decode_workspace_bytes(4, 30, 8, d, 4096, 0) == 0  # 30 % 8 != 0
 
