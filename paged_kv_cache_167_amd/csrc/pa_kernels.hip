@@ -292,14 +292,17 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(
   const int64_t row = i / kChunksPerRow;  // = t * Hkv + h
   const int h = static_cast<int>(row % num_kv_heads);
   const int64_t t = row / num_kv_heads;
+  // the row loads do not wait for the slot: all three are in flight together
+  const int64_t src = row * D + c * kE;
+  const u32x4 kx = load16(k + src);
+  const u32x4 vx = load16(v + src);
   const int64_t slot = slot_mapping[t];
   if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * D + c * kE;
-  const int64_t src = row * D + c * kE;
-  *reinterpret_cast<u32x4*>(k_cache + dst) = load16(k + src);
-  *reinterpret_cast<u32x4*>(v_cache + dst) = load16(v + src);
+  *reinterpret_cast<u32x4*>(k_cache + dst) = kx;
+  *reinterpret_cast<u32x4*>(v_cache + dst) = vx;
 }
 
 // ---------------------------------------------------------------------------
@@ -431,28 +434,45 @@ __device__ __forceinline__ void merge_row(T* dst, const float* rec_m, const floa
                                           const float* rec_o, int first, int npieces, int rec_rows,
                                           int g, int lane) {
   constexpr int kDPL = D / kWave;  // dims per lane
+  constexpr int kU = 4;            // piece outputs loaded together
   auto rec_of = [&](int p) { return p == 0 ? first * 2 + 1 : (first + p) * 2; };
+  auto out_of = [&](int p) { return rec_o + (static_cast<int64_t>(rec_of(p)) * rec_rows + g) * D; };
   float big_m = -INFINITY, den = 0.0f;
   float num[kDPL];
 #pragma unroll
   for (int k = 0; k < kDPL; ++k) num[k] = 0.0f;
   for (int p0 = 0; p0 < npieces; p0 += kWave) {
     const int p = p0 + lane;
+    const int cnt = min(kWave, npieces - p0);
     const int r = p < npieces ? rec_of(p) * rec_rows + g : 0;
     const float mp = p < npieces ? rec_m[r] : -INFINITY;
     const float lp = p < npieces ? rec_l[r] : 0.0f;
+    float ov[kU][kDPL];  // outputs of the first pieces, loaded alongside the maxima and sums
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int k = 0; k < kDPL; ++k) ov[u][k] = u < cnt ? out_of(p0 + u)[k * kWave + lane] : 0.0f;
     const float m_new = fmaxf(big_m, wave_max(mp));
     const float c_old = rescale(big_m, m_new);
     const float wp = p < npieces ? lp * __builtin_amdgcn_exp2f(mp - m_new) : 0.0f;
     den = den * c_old + wave_sum(wp);
 #pragma unroll
     for (int k = 0; k < kDPL; ++k) num[k] *= c_old;
-    const int cnt = min(kWave, npieces - p0);
-    for (int i = 0; i < cnt; ++i) {
-      const float wgt = as_f(__builtin_amdgcn_readlane(as_u(wp), i));
-      const float* o = rec_o + (static_cast<int64_t>(rec_of(p0 + i)) * rec_rows + g) * D;
+    for (int i = 0; i < cnt; i += kU) {
+      if (i > 0) {
 #pragma unroll
-      for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, o[k * kWave + lane], num[k]);
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int k = 0; k < kDPL; ++k) ov[u][k] = i + u < cnt ? out_of(p0 + i + u)[k * kWave + lane] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (i + u < cnt) {  // pieces in order
+          const float wgt = as_f(__builtin_amdgcn_readlane(as_u(wp), i + u));
+#pragma unroll
+          for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, ov[u][k], num[k]);
+        }
+      }
     }
     big_m = m_new;
   }
@@ -867,6 +887,24 @@ __device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], cons
   else read_stage_d64<VM, OFF>(ka, va, k, v, e0, e1, p0, p1);
 }
 
+// Six wave-uniform 32-bit loads through the scalar unit with a single wait.
+__device__ __forceinline__ void load_entries6(const int32_t* a0, const int32_t* a1, const int32_t* a2,
+                                              const int32_t* a3, const int32_t* a4, const int32_t* a5,
+                                              int32_t (&p)[6]) {
+  asm volatile(
+      "s_load_dword %[p0], %[a0], 0x0\n\t"
+      "s_load_dword %[p1], %[a1], 0x0\n\t"
+      "s_load_dword %[p2], %[a2], 0x0\n\t"
+      "s_load_dword %[p3], %[a3], 0x0\n\t"
+      "s_load_dword %[p4], %[a4], 0x0\n\t"
+      "s_load_dword %[p5], %[a5], 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [p0] "=&s"(p[0]), [p1] "=&s"(p[1]), [p2] "=&s"(p[2]), [p3] "=&s"(p[3]), [p4] "=&s"(p[4]),
+        [p5] "=&s"(p[5])
+      : [a0] "s"(a0), [a1] "s"(a1), [a2] "s"(a2), [a3] "s"(a3), [a4] "s"(a4), [a5] "s"(a5)
+      : "memory");
+}
+
 // Read a piece's q operand from LDS: chunks kb = 0 .. KB-1 at the lane's address + OFF +
 // 16 kb.  Called after the stage wait that covers the q loads; asm for the same reason
 // as the stage reads.
@@ -1166,21 +1204,30 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   // ---- main loop, unrolled by the ring depth so that stage offsets are immediates: the
   // fetch cursor runs NST - 1 tiles ahead; every step issues the same K/V loads.  The
   // table entries of the fetch cursor's tile are always loaded one step ahead.
+  // Prologue: the cursors of the first NST tiles, and all their table entries in one
+  // batch of scalar loads (one wait instead of one per tile).
+  static_assert(NST == 3, "the prologue loads the entries of three tiles");
   Cursor cf = cc;
+  Cursor c1 = cf;
+  wk.advance(c1);
+  Cursor c2 = c1;
+  wk.advance(c2);
   const int32_t *e0, *e1;
   int32_t pe0, pe1;
-  entry_ptrs(cf, 0 < n_my, e0, e1);
-  pe0 = scalar_load(e0);
-  pe1 = scalar_load(e1);
-  unroll<NST - 1>([&](auto stc) __attribute__((always_inline)) {
-    constexpr int st = decltype(stc)::value;
-    const bool real = st < n_my;
-    fbad[st] = fetch(cf, real, real && (st == 0 || cf.t == 0), st, pe0, pe1);
-    wk.advance(cf);
-    entry_ptrs(cf, st + 1 < n_my, e0, e1);
-    pe0 = scalar_load(e0);
-    pe1 = scalar_load(e1);
-  });
+  {
+    const int32_t *a0, *a1, *b0, *b1;
+    entry_ptrs(cf, 0 < n_my, a0, a1);
+    entry_ptrs(c1, 1 < n_my, b0, b1);
+    entry_ptrs(c2, 2 < n_my, e0, e1);
+    int32_t p[6];
+    load_entries6(uniform_ptr(a0), uniform_ptr(a1), uniform_ptr(b0), uniform_ptr(b1), uniform_ptr(e0),
+                  uniform_ptr(e1), p);
+    fbad[0] = fetch(cf, 0 < n_my, 0 < n_my, 0, p[0], p[1]);
+    fbad[1] = fetch(c1, 1 < n_my, 1 < n_my && c1.t == 0, 1, p[2], p[3]);
+    cf = c2;
+    pe0 = p[4];
+    pe1 = p[5];
+  }
   for (int i0 = 0; i0 < n_my; i0 += NST) {
     unroll<NST>([&](auto stc) __attribute__((always_inline)) {
       constexpr int st = decltype(stc)::value;
@@ -1215,18 +1262,18 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
   T* dst = out + (static_cast<int64_t>(s) * num_q_heads + h) * D;
-  const int ctx = context_lens[s];
+  const int kvh = h / group;
+  const int gtile = (h - kvh * group) / GT;
+  const int g = h - kvh * group - gtile * GT;
+  const int n_units = (num_q_heads / group) * n_gtiles;
+  const int ctx = context_lens[s];  // both loads in flight together
+  const int2 d = seg_desc[s * n_units + kvh * n_gtiles + gtile];
   if (ctx <= 0 || ctx > max_context_len) {  // nothing to attend over: zeros; invalid: NaN
     const T fill = static_cast<T>(ctx == 0 ? 0.0f : __builtin_nanf(""));
 #pragma unroll
     for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = fill;
     return;
   }
-  const int kvh = h / group;
-  const int gtile = (h - kvh * group) / GT;
-  const int g = h - kvh * group - gtile * GT;
-  const int n_units = (num_q_heads / group) * n_gtiles;
-  const int2 d = seg_desc[s * n_units + kvh * n_gtiles + gtile];
   if (d.x == d.y) return;  // one wave held the whole segment and wrote the row
   if (d.x < 0 || d.x > d.y || d.y >= w_cap) {  // not written by the stream kernel: no records
 #pragma unroll
