@@ -45,9 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama3_8b",
-                    choices=["llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
-                             "long_context_b16", "long_context_b32", "tiny_fp32"])
+    ap.add_argument("--config", default="llama3_8b", choices=ALL_CONFIGS + ["all"],
+                    help="workload; 'all' runs every one in turn, one JSON line each")
     ap.add_argument("--partition", type=int, default=0,
                     help="partition size in tokens (0: one wave per resident slot; >0: more "
                          "waves, each taking at most about that many tokens)")
@@ -58,6 +57,19 @@ def parse():
                     help="first run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic that scales the HBM byte counters)")
     return ap.parse_args()
+
+
+ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
+               "long_context_b16", "long_context_b32"]
+WORKLOAD_NAMES = {
+    "tiny_fp32": "tiny fp32 decode (4 sequences, ctx 1..250)",
+    "llama3_8b": "Llama-3-8B-shaped decode layer",
+    "llama2_70b": "Llama-2-70B-shaped 8K-context decode layer",
+    "shared_prefix": "parallel sampling with shared prompt blocks",
+    "long_context_b8": "32K-128K context decode, block size 8",
+    "long_context_b16": "32K-128K context decode, block size 16",
+    "long_context_b32": "32K-128K context decode, block size 32",
+}
 
 
 def make_case(name):
@@ -122,19 +134,30 @@ def main():
               "(decode shards by sequence or by kv head with no exchange between GPUs)",
               file=sys.stderr)
         sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import workloads
+    workloads.set_progress(log)
+    for name in (ALL_CONFIGS if args.config == "all" else [args.config]):
+        result = run_one(args, name)
+        print(json.dumps(result), flush=True)
+        torch.cuda.empty_cache()
+
+
+def run_one(args, config):
+    """Measure one workload; returns the result line as a dict."""
     import numpy as np
     import torch
 
     import paged_kv_cache_167_amd as P
-    if not torch.cuda.is_available():
-        print("no GPU visible", file=sys.stderr)
-        sys.exit(1)
     dev = torch.device("cuda:0")
     partition = args.partition
 
-    log(f"generating workload {args.config}")
+    log(f"generating workload {config}")
     t_gen = time.time()
-    case = make_case(args.config)
+    case = make_case(config)
     log(f"  {time.time() - t_gen:.1f} s; {case.num_seqs} seqs, kv bytes/step {case.kv_bytes()/1e9:.3f} GB")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     q, tables, ctx = t(case.q), t(case.block_tables), t(case.context_lens)
@@ -196,6 +219,25 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     kern_ms_avg = e0.elapsed_time(e1) / args.steps
+
+    # pa_decode (both launches) and pa_cache_write, each the same way
+    def decode_only():
+        P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
+                    case.num_kv_heads, max_context_len=mcl, partition_size=partition,
+                    workspace=ws, stream=stream)
+
+    def write_only():
+        P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
+
+    per_call_ms = {}
+    for key, fn in (("decode", decode_only), ("write", write_only)):
+        fn()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per_call_ms[key] = e0.elapsed_time(e1) / args.steps
     step()  # leave the rows pa_decode writes in out
     torch.cuda.synchronize()
 
@@ -222,7 +264,9 @@ def main():
     achieved = alg_bytes / (kern_ms_avg * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kernel = stream_kernel_name(case.dtype == np.float16)
-    traffic = measured_traffic(kernel, args.config, partition)
+    traffic = measured_traffic(kernel, config, partition)
+    unique = case.unique_kv_bytes() if config == "shared_prefix" else kv_bytes
+    write_bytes = 2 * 2 * case.num_seqs * case.num_kv_heads * case.head_dim * case.elt_bytes
 
     result = {
         "metric": "paged decode KV GB/s and % of MI355X HBM peak; sequences/s per layer",
@@ -238,7 +282,7 @@ def main():
         "dtype": "f16" if case.dtype == np.float16 else "f32",
         "data": "synthetic",
         "config": {
-            "workload": {"llama3_8b": "Llama-3-8B-shaped decode layer"}.get(args.config, args.config),
+            "workload": WORKLOAD_NAMES[config], "name": config,
             "num_seqs": case.num_seqs, "num_q_heads": case.num_q_heads,
             "num_kv_heads": case.num_kv_heads, "head_dim": case.head_dim,
             "block_size": case.block_size, "num_blocks": case.num_blocks,
@@ -248,6 +292,19 @@ def main():
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "pa_decode": {
+            "us": round(per_call_ms["decode"] * 1e3, 2),
+            "kv_gbs": round(kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100.0 * kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "unique_kv_bytes": unique,
+            "unique_kv_gbs": round(unique / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
+            "seqs_per_s_per_layer": round(case.num_seqs / (per_call_ms["decode"] * 1e-3), 1),
+        },
+        "pa_cache_write": {
+            "us": round(per_call_ms["write"] * 1e3, 2),
+            "gbs": round(write_bytes / (per_call_ms["write"] * 1e-3) / 1e9, 2),
+            "bytes": write_bytes,
+        },
         "roofline": {
             "kernel": kernel,
             "bound": "hbm",
@@ -265,7 +322,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case)
-    print(json.dumps(result), flush=True)
+    del k_cache, v_cache, ws
+    return result
 
 
 if __name__ == "__main__":

@@ -266,6 +266,13 @@ def _tables_from(allocator: BlockAllocator, blocks_per_seq, width: int) -> np.nd
 # ---------------------------------------------------------------------------
 
 _LOGICAL_MEMO = {}  # one entry: the last logical data set (lets block-size sweeps reuse it)
+_PROGRESS = None    # optional callable(message): told as each sequence's data is generated
+
+
+def set_progress(fn) -> None:
+    """Report generation progress through fn(message) (None: silent)."""
+    global _PROGRESS
+    _PROGRESS = fn
 
 
 def _logical_data(lseed, ctx, num_q_heads, num_kv_heads, head_dim, sigma, dtype, variant):
@@ -292,6 +299,8 @@ def _logical_data(lseed, ctx, num_q_heads, num_kv_heads, head_dim, sigma, dtype,
         elif variant == "poscode":
             _poscode(v, 0, denom, dtype)
         logical.append((k, v))
+        if _PROGRESS is not None:
+            _PROGRESS(f"sequence {s + 1}/{len(ctx)}: {c} tokens generated")
     _LOGICAL_MEMO[key] = (q, logical)
     return q, logical
 
