@@ -325,3 +325,52 @@ def test_long_context_block_sizes_agree():
         ref = O.decode_one(case.q, kc, vc, case.block_tables, case.context_lens, case.scale,
                            case.block_size, case.num_kv_heads, 0, h)
         G.assert_close(outs[16][0, h], ref, case.dtype, f"long_context seq0 head {h}")
+
+
+# ------------------------------------------------------------------ extreme sizes
+def test_many_short_sequences():
+    """2000 sequences of 1..80 tokens (past the 256-sequence register index), some of them
+    emptied on the device: every row against the oracle, empty rows exactly zero."""
+    torch = _torch()
+    rng = np.random.default_rng(2000)
+    ctx = rng.integers(1, 80, size=2000, endpoint=True)
+    case = W.make_case(seed=2001, dtype=np.float16, context_lens=ctx, num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, sigma=0.5)
+    d = G.to_device(case)
+    zero = np.array([0, 7, 1999, 1024])
+    ctx_dev = d.ctx.clone()
+    ctx_dev[torch.from_numpy(zero).cuda()] = 0
+    G.say("2000 sequences: decode")
+    got = G.decode(case, d, ctx=ctx_dev)
+    assert np.all(got[zero] == 0)
+    kc, vc = oracle_pools(case)
+    ref = oracle_decode(case, kc, vc)
+    keep = np.setdiff1d(np.arange(case.num_seqs), zero)
+    G.assert_close(got[keep], ref[keep], case.dtype, "2000 sequences")
+    _fp16_bound(got[keep], ref[keep], case, "2000 sequences")
+
+
+def test_one_context_split_over_every_wave():
+    """One 200K-token context (GQA 8): the default split cuts it into about a thousand
+    pieces that the reduce merges; against the oracle."""
+    case = W.make_case(seed=2002, dtype=np.float16, context_lens=[200_000], num_q_heads=8,
+                       num_kv_heads=1, head_dim=128, block_size=16, sigma=0.5)
+    d = G.to_device(case)
+    G.say("200K context: decode")
+    got = G.decode(case, d)
+    kc, vc = oracle_pools(case)
+    ref = oracle_decode(case, kc, vc)
+    G.assert_close(got, ref, case.dtype, "200K context")
+    _fp16_bound(got, ref, case, "200K context")
+
+
+def test_more_waves_than_the_gpu_holds():
+    """A 32-token partition asks for about 4500 waves, several per resident slot: results
+    agree with the oracle and, within rounding, with the default split."""
+    case = _mid_case()
+    d = G.to_device(case)
+    got = G.decode(case, d, partition_size=32)
+    kc, vc = oracle_pools(case)
+    ref = oracle_decode(case, kc, vc)
+    G.assert_close(got, ref, case.dtype, "partition 32")
+    _within_rounding(got, G.decode(case, d), case.dtype, "partition 32 vs default", _vmax(case))
