@@ -38,7 +38,10 @@ Readings where the pages are silent (each listed in the design notes):
 
 Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 (worked example from [DRV] section 6, brute force, torch SDPA on contiguous
-K/V, permutation / block-size / sharing invariants, closed forms).
+K/V, permutation / block-size / sharing invariants, closed forms); the FP8 part
+([CON] section 6) by ``tests/test_oracle_fp8.py`` (code values fixed by the E4M3
+definition, torch's float8_e4m3fn table and rounding, brute-force nearest code,
+ties, saturation, and lossless round trips that reduce FP8 decode to the fp64 one).
 """
 
 from __future__ import annotations
@@ -253,3 +256,86 @@ def decode_one_partitioned(q, k_cache, v_cache, block_tables, context_lens, scal
         num += w * o_p
         den += w
     return num / den
+
+
+# ---------------------------------------------------------------------------
+# FP8 KV cache  ([CON] section 6: the blocks hold compressed K/V and the kernel
+# dequantizes them).  The pages name FP8 but no format or scaling; the reading
+# taken: the OCP FP8 E4M3 format (4 exponent bits, bias 7, 3 mantissa bits, no
+# infinities, the all-ones exponent with mantissa 7 is NaN, largest finite 448),
+# one scale for all of K and one for all of V.  Storing x means the code nearest
+# to x / scale (ties to an even code, i.e. an even mantissa), saturated to +-448;
+# loading a code means its value times the scale.
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of one FP8 E4M3 code, from the format's definition."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    exponent = (code >> 3) & 0xF
+    mantissa = code & 0x7
+    if exponent == 0xF and mantissa == 0x7:
+        return math.nan
+    if exponent == 0:  # subnormal: mantissa/8 * 2^(1 - bias)
+        return sign * (mantissa / 8.0) * 2.0 ** -6
+    return sign * (1.0 + mantissa / 8.0) * 2.0 ** (exponent - 7)
+
+
+E4M3_TABLE = np.array([e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of an array of codes (uint8), float64."""
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Nearest FP8 E4M3 code of each value (ties to the even code), saturating at +-448.
+
+    The positive finite codes 0x00..0x7E have increasing values; the magnitude is
+    clamped to 448 and matched against that list, and the sign bit is the sign of x
+    (so -0.0 gives 0x80).  NaN gives the NaN code with x's sign.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    pos = E4M3_TABLE[:0x7F]  # codes 0x00..0x7E, values 0 .. 448 increasing
+    mag = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.clip(np.searchsorted(pos, mag, side="left"), 0, 0x7E)  # first value >= mag
+    lo = np.maximum(hi - 1, 0)
+    d_lo = mag - pos[lo]
+    d_hi = pos[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    code = np.where(np.isnan(x), np.uint8(0x7F), code)
+    return (code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+
+
+def fp8_inverse_scale(scale: float) -> np.float32:
+    """The single-precision reciprocal 1/scale that the store multiplies by (rounded once)."""
+    return np.float32(1.0 / float(scale))
+
+
+def cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, block_size: int, k_scale: float,
+                    v_scale: float):
+    """Like cache_write, but each stored element is the E4M3 code of x / scale.
+
+    The quotient is taken the way the store takes it: x (fp16) times the
+    single-precision 1/scale, as one single-precision product.
+    """
+    kq = e4m3_encode(np.asarray(k, dtype=np.float32) * fp8_inverse_scale(k_scale))
+    vq = e4m3_encode(np.asarray(v, dtype=np.float32) * fp8_inverse_scale(v_scale))
+    return cache_write(kq, vq, slot_mapping, k_cache, v_cache, block_size)
+
+
+def dequantize_pool(codes, scale: float) -> np.ndarray:
+    """float64 pool of code values times the scale (the load of [CON] section 6)."""
+    return e4m3_decode(codes) * float(scale)
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale: float, v_scale: float, block_tables,
+               context_lens, scale: float, block_size: int, num_kv_heads: int) -> np.ndarray:
+    """Attention over the dequantized pools: the plain definition, unchanged."""
+    return decode(q, dequantize_pool(k_codes, k_scale), dequantize_pool(v_codes, v_scale),
+                  block_tables, context_lens, scale, block_size, num_kv_heads)
