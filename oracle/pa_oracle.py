@@ -265,7 +265,8 @@ def decode_one_partitioned(q, k_cache, v_cache, block_tables, context_lens, scal
 # infinities, the all-ones exponent with mantissa 7 is NaN, largest finite 448),
 # one scale for all of K and one for all of V.  Storing x means the code nearest
 # to x / scale (ties to an even code, i.e. an even mantissa), saturated to +-448;
-# loading a code means its value times the scale.
+# a NaN is stored as 0x7F whatever its sign bit (a NaN's sign carries no value,
+# and arithmetic need not keep it); loading a code means its value times the scale.
 # ---------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
@@ -297,7 +298,7 @@ def e4m3_encode(x) -> np.ndarray:
 
     The positive finite codes 0x00..0x7E have increasing values; the magnitude is
     clamped to 448 and matched against that list, and the sign bit is the sign of x
-    (so -0.0 gives 0x80).  NaN gives the NaN code with x's sign.
+    (so -0.0 gives 0x80).  NaN gives 0x7F.
     """
     x = np.asarray(x, dtype=np.float64)
     pos = E4M3_TABLE[:0x7F]  # codes 0x00..0x7E, values 0 .. 448 increasing
@@ -308,8 +309,8 @@ def e4m3_encode(x) -> np.ndarray:
     d_hi = pos[hi] - mag
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    code = np.where(np.isnan(x), np.uint8(0x7F), code)
-    return (code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+    code = code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
 def fp8_inverse_scale(scale: float) -> np.float32:
