@@ -60,7 +60,8 @@ def parse():
 
 
 ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
-               "long_context_b16", "long_context_b32"]
+               "long_context_b16", "long_context_b32", "llama3_8b_fp8", "llama2_70b_fp8",
+               "long_context_b16_fp8"]
 WORKLOAD_NAMES = {
     "tiny_fp32": "tiny fp32 decode (4 sequences, ctx 1..250)",
     "llama3_8b": "Llama-3-8B-shaped decode layer",
@@ -69,11 +70,17 @@ WORKLOAD_NAMES = {
     "long_context_b8": "32K-128K context decode, block size 8",
     "long_context_b16": "32K-128K context decode, block size 16",
     "long_context_b32": "32K-128K context decode, block size 32",
+    "llama3_8b_fp8": "Llama-3-8B-shaped decode layer, FP8 E4M3 KV cache",
+    "llama2_70b_fp8": "Llama-2-70B-shaped 8K-context decode layer, FP8 E4M3 KV cache",
+    "long_context_b16_fp8": "32K-128K context decode, block size 16, FP8 E4M3 KV cache",
 }
+FP8_SUFFIX = "_fp8"
 
 
 def make_case(name):
     import workloads as W
+    if name.endswith(FP8_SUFFIX):  # the same tokens, stored as E4M3 codes
+        name = name[:-len(FP8_SUFFIX)]
     if name.startswith("long_context_b"):
         return W.long_context(int(name.rsplit("b", 1)[1]))
     return W.CONFIGS[name]()
@@ -98,29 +105,52 @@ def measured_traffic(kernel, config, partition):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case):
+def fp8_scales(case):
+    """Per-tensor E4M3 scales: the largest |k| (|v|) of the workload maps to 448."""
+    import numpy as np
+    f = lambda a, b: float(np.float32(max(np.abs(a.astype(np.float32)).max(initial=0.0),  # noqa: E731
+                                          np.abs(b.astype(np.float32)).max(initial=0.0)) / 448.0))
+    return f(case.prefix_k, case.new_k), f(case.prefix_v, case.new_v)
+
+
+def cpu_baseline(case, fp8=False):
     """The oracle, as it stands, on the same workload: write the new tokens, then decode."""
+    import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import pa_oracle as O
     log("cpu baseline: building the oracle's pools (not timed)")
-    kc, vc = O.cache_write(case.prefix_k, case.prefix_v, case.prefix_slots, case.empty_pool(),
-                           case.empty_pool(), case.block_size)
+    if fp8:
+        ks, vs = fp8_scales(case)
+        empty = np.full(case.empty_pool().shape, 0x7F, dtype=np.uint8)
+        kc, vc = O.cache_write_fp8(case.prefix_k, case.prefix_v, case.prefix_slots, empty,
+                                   empty.copy(), case.block_size, ks, vs)
+    else:
+        kc, vc = O.cache_write(case.prefix_k, case.prefix_v, case.prefix_slots, case.empty_pool(),
+                               case.empty_pool(), case.block_size)
+    elt = 1 if fp8 else case.elt_bytes
+    kv_all = int(case.context_lens.astype("int64").sum()) * case.num_kv_heads * case.head_dim * 2
     n = case.num_seqs
-    if case.kv_bytes() > 1.5e9:  # keep the CPU leg to tens of seconds: a prefix of the batch
-        n = max(1, int(n * 1.5e9 / case.kv_bytes()))
+    if kv_all * case.elt_bytes > 1.5e9:  # keep the CPU leg to tens of seconds: a prefix of the batch
+        n = max(1, int(n * 1.5e9 / (kv_all * case.elt_bytes)))
     reps = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         while reps == 0 or time.perf_counter() - t0 < 10.0:  # about 10 s of CPU work
-            kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc, vc,
-                                     case.block_size)
-            O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n],
-                     case.scale, case.block_size, case.num_kv_heads)
+            if fp8:
+                kc2, vc2 = O.cache_write_fp8(case.new_k[:n], case.new_v[:n], case.new_slots[:n],
+                                             kc, vc, case.block_size, ks, vs)
+                O.decode_fp8(case.q[:n], kc2, vc2, ks, vs, case.block_tables[:n],
+                             case.context_lens[:n], case.scale, case.block_size, case.num_kv_heads)
+            else:
+                kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc,
+                                         vc, case.block_size)
+                O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n],
+                         case.scale, case.block_size, case.num_kv_heads)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
     kv = int(case.context_lens[:n].astype("int64").sum()) * case.num_kv_heads * case.head_dim * \
-        2 * case.elt_bytes
+        2 * elt
     return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds_per_step": dt, "steps": reps, "seqs_per_s": n / dt,
             "sample": f"{n} of {case.num_seqs} sequences, {reps} steps (write new tokens + "
@@ -155,18 +185,28 @@ def run_one(args, config):
     dev = torch.device("cuda:0")
     partition = args.partition
 
+    fp8 = config.endswith(FP8_SUFFIX)
     log(f"generating workload {config}")
     t_gen = time.time()
     case = make_case(config)
-    log(f"  {time.time() - t_gen:.1f} s; {case.num_seqs} seqs, kv bytes/step {case.kv_bytes()/1e9:.3f} GB")
+    elt = 1 if fp8 else case.elt_bytes  # bytes per stored K/V element
+    kv_bytes = int(case.context_lens.astype(np.int64).sum()) * case.num_kv_heads * \
+        case.head_dim * 2 * elt
+    log(f"  {time.time() - t_gen:.1f} s; {case.num_seqs} seqs, kv bytes/step {kv_bytes/1e9:.3f} GB")
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
     q, tables, ctx = t(case.q), t(case.block_tables), t(case.context_lens)
     shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
-    tdt = torch.float16 if case.dtype == np.float16 else torch.float32
-    k_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
-    v_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
     pk, pv, ps = t(case.prefix_k), t(case.prefix_v), t(case.prefix_slots)
-    P.pa_cache_write(pk, pv, ps, k_cache, v_cache)
+    if fp8:
+        k_scale, v_scale = fp8_scales(case)
+        k_cache = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)  # unwritten: NaN code
+        v_cache = torch.full(shape, 0x7F, dtype=torch.uint8, device=dev)
+        P.pa_cache_write_fp8(pk, pv, ps, k_cache, v_cache, k_scale, v_scale)
+    else:
+        tdt = torch.float16 if case.dtype == np.float16 else torch.float32
+        k_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+        v_cache = torch.full(shape, float("nan"), dtype=tdt, device=dev)
+        P.pa_cache_write(pk, pv, ps, k_cache, v_cache)
     del pk, pv, ps
     new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
     out = torch.empty_like(q)
@@ -183,16 +223,37 @@ def run_one(args, config):
         torch.cuda.synchronize()
         del src, dst
 
+    def write_only():
+        if fp8:
+            P.pa_cache_write_fp8(new_k, new_v, new_slots, k_cache, v_cache, k_scale, v_scale,
+                                 stream=stream)
+        else:
+            P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
+
+    def decode_only():
+        if fp8:
+            P.pa_decode_fp8(out, q, k_cache, v_cache, tables, ctx, case.scale, k_scale, v_scale,
+                            case.block_size, case.num_kv_heads, max_context_len=mcl,
+                            partition_size=partition, workspace=ws, stream=stream)
+        else:
+            P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
+                        case.num_kv_heads, max_context_len=mcl, partition_size=partition,
+                        workspace=ws, stream=stream)
+
     def step():
-        P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
-        P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
-                    case.num_kv_heads, max_context_len=mcl, partition_size=partition,
-                    workspace=ws, stream=stream)
+        write_only()
+        decode_only()
 
     def stream_kernel():  # the first of pa_decode's two launches, on its own
-        P.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale,
-                               case.block_size, case.num_kv_heads, max_context_len=mcl,
-                               partition_size=partition, workspace=ws, stream=stream)
+        if fp8:
+            P.pa_decode_fp8_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale, k_scale,
+                                       v_scale, case.block_size, case.num_kv_heads,
+                                       max_context_len=mcl, partition_size=partition,
+                                       workspace=ws, stream=stream)
+        else:
+            P.pa_decode_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale,
+                                   case.block_size, case.num_kv_heads, max_context_len=mcl,
+                                   partition_size=partition, workspace=ws, stream=stream)
 
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -221,14 +282,6 @@ def run_one(args, config):
     kern_ms_avg = e0.elapsed_time(e1) / args.steps
 
     # pa_decode (both launches) and pa_cache_write, each the same way
-    def decode_only():
-        P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
-                    case.num_kv_heads, max_context_len=mcl, partition_size=partition,
-                    workspace=ws, stream=stream)
-
-    def write_only():
-        P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
-
     per_call_ms = {}
     for key, fn in (("decode", decode_only), ("write", write_only)):
         fn()
@@ -256,7 +309,6 @@ def run_one(args, config):
             cold_ms.append(e0.elapsed_time(e1))
         del flush
 
-    kv_bytes = case.kv_bytes()
     tokens_blocks = int(sum(-(-int(c) // case.block_size) for c in case.context_lens))
     q_bytes = case.num_seqs * case.num_q_heads * case.head_dim * case.elt_bytes
     # K/V rows, q in, out, the table entries in use and the context lengths
@@ -266,7 +318,8 @@ def run_one(args, config):
     kernel = stream_kernel_name(case.dtype == np.float16)
     traffic = measured_traffic(kernel, config, partition)
     unique = case.unique_kv_bytes() if config == "shared_prefix" else kv_bytes
-    write_bytes = 2 * 2 * case.num_seqs * case.num_kv_heads * case.head_dim * case.elt_bytes
+    # fp16 (or fp32) rows in, stored rows out
+    write_bytes = 2 * case.num_seqs * case.num_kv_heads * case.head_dim * (case.elt_bytes + elt)
 
     result = {
         "metric": "paged decode KV GB/s and % of MI355X HBM peak; sequences/s per layer",
@@ -289,6 +342,7 @@ def run_one(args, config):
             "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}, "
                             f"sum {int(case.context_lens.sum())}",
             "partition_size": partition, "kv_bytes_per_step": kv_bytes,
+            "kv_cache": "e4m3" if fp8 else ("f16" if case.dtype == np.float16 else "f32"),
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
@@ -321,7 +375,7 @@ def run_one(args, config):
         },
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(case)
+        result["cpu_baseline"] = cpu_baseline(case, fp8)
     del k_cache, v_cache, ws
     return result
 

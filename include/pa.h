@@ -19,6 +19,8 @@
  *  [SOSP] "《Efficient Memory Management for LLM Serving with PagedAttention》深度解读报告"
  *         (zako-mio.github.io), sections 2.3, 3.2-3.4 (K and V blocks kept apart; the
  *         fill count keeps padding out; write the new token, then attend over all valid KV).
+ *         [CON] section 6 adds FP8 storage inside the blocks, expanded by the kernel:
+ *         the *_fp8 calls below.
  *
  * Layouts (all row-major, contiguous, 16-byte aligned):
  *   k_cache, v_cache  [num_blocks, num_kv_heads, block_size, head_dim]   (one layer)
@@ -31,6 +33,8 @@
  * Query head h attends with kv head h / (num_q_heads / num_kv_heads).
  * Supported: dtype PA_F32 or PA_F16 (all of q, k, v, caches and out share it;
  * arithmetic is fp32), head_dim 64 or 128, block_size 8, 16 or 32.
+ * The *_fp8 calls keep the pools as one byte per element (FP8 E4M3 codes) with q, k,
+ * v and out in fp16; same layouts, same head_dim and block_size support.
  */
 #ifndef PA_H
 #define PA_H
@@ -158,12 +162,61 @@ int pa_decode_reduce(void* out, const int32_t* context_lens,
                      int32_t max_context_len, int32_t partition_size, int32_t dtype,
                      const void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * FP8 KV cache ([CON] section 6: blocks store K/V compressed, the kernel expands them).
+ *
+ * The pages name FP8 but no format or scaling; these calls take the OCP E4M3 format
+ * (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite 448; S.1111.111
+ * is NaN; no infinities) and one scale for all of K and one for all of V.  A stored code
+ * c of the K pool means value(c) * k_scale, likewise for V.
+ *
+ * pa_cache_write_fp8 -- pa_cache_write for E4M3 pools: element x of k[t, h, :] (fp16)
+ * is stored as the code nearest to y = x * (1/k_scale), where 1/k_scale is rounded once
+ * to fp32 and y is one fp32 product; ties go to the even code, |y| beyond 448 saturates
+ * to +-448 (code 0x7E / 0xFE), any NaN gives 0x7F.  Same for v with v_scale.
+ * Slot handling, skips and races are those of pa_cache_write.
+ *
+ * k, v              device, [num_tokens, num_kv_heads, head_dim] fp16
+ * k_cache, v_cache  device, [num_blocks, num_kv_heads, block_size, head_dim] uint8; updated in place
+ * k_scale, v_scale  positive, finite
+ * returns PA_OK, or a negative code with nothing launched.
+ */
+int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping,
+                       void* k_cache, void* v_cache, float k_scale, float v_scale,
+                       int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int64_t num_blocks, void* stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over E4M3 pools: the result is attention over the
+ * dequantized K and V (every code times its scale), everything else as pa_decode with
+ * dtype PA_F16 (q and out fp16, the same workspace size query and work split).  The
+ * codes are expanded to fp16 exactly; k_scale joins the softmax scale (scale * k_scale
+ * must be a positive finite fp32 value) and v_scale multiplies the normalised output.
+ * The probabilities are rounded to fp16 for the P.V product, as in pa_decode.
+ * pa_decode_fp8_partitions is its first launch alone; pa_decode_reduce with dtype PA_F16
+ * is the second.  A NaN code inside a context makes the affected rows NaN.
+ */
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens,
+                  float scale, float k_scale, float v_scale, int32_t block_size,
+                  int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                  int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                  int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens,
+                             float scale, float k_scale, float v_scale, int32_t block_size,
+                             int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                             int64_t num_blocks, int32_t partition_size,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* Description of the last error on the calling thread ("" if none); valid until the next call. */
 const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 0)
+#define PA_ABI_VERSION ((2 << 16) | 1)
 
 #ifdef __cplusplus
 }

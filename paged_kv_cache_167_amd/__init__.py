@@ -11,7 +11,10 @@ from ._lib import (  # noqa: F401
     last_error,
     lib,
     pa_cache_write,
+    pa_cache_write_fp8,
     pa_decode,
+    pa_decode_fp8,
+    pa_decode_fp8_partitions,
     pa_decode_partitions,
     pa_decode_reduce,
     pa_decode_workspace_bytes,

@@ -43,6 +43,15 @@ SIGNATURES = {
                                         _c_int64, _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_reduce": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                     _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_cache_write_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
+                                      _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
+    "pa_decode_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
+                                 ctypes.c_float, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                 _c_int32, _c_int32, _c_int64, _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_fp8_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                            ctypes.c_float, ctypes.c_float, _c_int32, _c_int32,
+                                            _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                            _c_int64, _c_int32, _vp, ctypes.c_size_t, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_c_int32, []),
 }
@@ -175,3 +184,59 @@ def pa_decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition
                                   int(partition_size), _dtype_code(out), ws_ptr, ws_bytes,
                                   _stream(out, stream))
     _check("pa_decode_reduce", code)
+
+
+def _require_codes(t, name):
+    import torch
+    if t.dtype != torch.uint8:
+        raise PaError("binding", PA_ERR_UNSUPPORTED, f"{name} must hold E4M3 codes as uint8")
+
+
+def pa_cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stream=None) -> None:
+    """E4M3 pools (uint8): k_cache[slot // B, :, slot % B] = code(k[t] / k_scale), same for v."""
+    import torch
+    _require_codes(k_cache, "k_cache")
+    _require_codes(v_cache, "v_cache")
+    if k.dtype != torch.float16 or v.dtype != torch.float16:
+        raise PaError("binding", PA_ERR_UNSUPPORTED, "k and v must be float16")
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    code = lib().pa_cache_write_fp8(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), float(k_scale),
+        float(v_scale), k.shape[0], num_kv_heads, head_dim, block_size, num_blocks,
+        _stream(k_cache, stream))
+    _check("pa_cache_write_fp8", code)
+
+
+def _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                     block_size, num_kv_heads, max_context_len, partition_size, workspace, stream):
+    _require_codes(k_cache, "k_cache")
+    _require_codes(v_cache, "v_cache")
+    args, workspace = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   block_size, num_kv_heads, max_context_len, partition_size,
+                                   workspace, stream)
+    if args[16] != PA_F16:
+        raise PaError("binding", PA_ERR_UNSUPPORTED, "q and out must be float16 with E4M3 pools")
+    # (out, q, kc, vc, bt, ctx, scale, k_scale, v_scale, block_size, ...) without the dtype
+    return args[:7] + (float(k_scale), float(v_scale)) + args[7:16] + args[17:], workspace
+
+
+def pa_decode_fp8(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                  block_size, num_kv_heads, max_context_len=None, partition_size=DEFAULT_PARTITION,
+                  workspace=None, stream=None):
+    """pa_decode over E4M3 pools: attention over the codes times k_scale / v_scale."""
+    args, workspace = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                       k_scale, v_scale, block_size, num_kv_heads, max_context_len,
+                                       partition_size, workspace, stream)
+    _check("pa_decode_fp8", lib().pa_decode_fp8(*args))
+    return workspace
+
+
+def pa_decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                             v_scale, block_size, num_kv_heads, max_context_len=None,
+                             partition_size=DEFAULT_PARTITION, workspace=None, stream=None):
+    """First launch of pa_decode_fp8; pa_decode_reduce (dtype float16) is the second."""
+    args, workspace = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                       k_scale, v_scale, block_size, num_kv_heads, max_context_len,
+                                       partition_size, workspace, stream)
+    _check("pa_decode_fp8_partitions", lib().pa_decode_fp8_partitions(*args))
+    return workspace

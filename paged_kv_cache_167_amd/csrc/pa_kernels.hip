@@ -59,11 +59,14 @@ namespace {
 using f16 = _Float16;
 typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kMaxWaves = 4096;  // persistent fp32 waves in the default split
 constexpr int kMfWavesPerCU = 4;  // persistent fp16 waves per compute unit in the default split
 constexpr int kMfStages = 3;      // LDS ring depth of the fp16 kernel
+constexpr int kF8WavesPerCU = 4;  // the same for the kernel over E4M3 pools
+constexpr int kF8Stages = 3;
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -305,6 +308,67 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(
   *reinterpret_cast<u32x4*>(v_cache + dst) = vx;
 }
 
+// E4M3 code of y: the nearest value (ties to an even code), saturated to +-448; any
+// NaN becomes 0x7F (its sign is not kept: the multiply before need not keep it).  Normal range: round the fp32 bit pattern
+// to 3 mantissa bits (a carry moves into the exponent) and rebase the exponent from
+// bias 127 to 7.  Below 2^-6 the codes are steps of 2^-9: round y * 2^9 to an integer.
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t bits = as_u(y);
+  const uint32_t sign = (bits >> 24) & 0x80u;
+  const uint32_t mag = bits & 0x7FFFFFFFu;
+  const float a = as_f(mag);
+  uint32_t c;
+  if (mag > 0x7F800000u) return 0x7Fu;
+  if (a >= 448.0f) {
+    c = 0x7Eu;
+  } else if (a >= 0.015625f) {
+    c = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
+  } else {
+    c = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  }
+  return c | sign;
+}
+
+// Eight fp16 values times inv, as eight E4M3 codes (byte i = element i).
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, float inv) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f16x2 h = word_as<f16x2>(x, i / 2);
+    const float y = static_cast<float>(h[i % 2]) * inv;
+    w[i / 4] |= e4m3_code(y) << (8 * (i % 4));
+  }
+  return u32x2{w[0], w[1]};
+}
+
+// E4M3 pools: one thread per 16 codes (two 16-byte fp16 chunks) of one (token, kv head)
+// row.  Each element is stored as the code of x * inv_scale, one fp32 product.
+template <int D>
+__global__ __launch_bounds__(256) void pa_cache_write_fp8_kernel(
+    const f16* __restrict__ k, const f16* __restrict__ v, const int64_t* __restrict__ slot_mapping,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float k_inv, float v_inv,
+    int64_t num_chunks, int num_kv_heads, int block_size, int64_t num_slots) {
+  constexpr int kChunksPerRow = D / 16;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= num_chunks) return;
+  const int c = static_cast<int>(i % kChunksPerRow);
+  const int64_t row = i / kChunksPerRow;  // = t * Hkv + h
+  const int h = static_cast<int>(row % num_kv_heads);
+  const int64_t t = row / num_kv_heads;
+  const int64_t src = row * D + c * 16;
+  const u32x4 k0 = load16(k + src), k1 = load16(k + src + 8);
+  const u32x4 v0 = load16(v + src), v1 = load16(v + src + 8);
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;  // padding, or outside the pool
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * D + c * 16;
+  const u32x2 ka = encode8(k0, k_inv), kb = encode8(k1, k_inv);
+  const u32x2 va = encode8(v0, v_inv), vb = encode8(v1, v_inv);
+  *reinterpret_cast<u32x4*>(k_cache + dst) = u32x4{ka[0], ka[1], kb[0], kb[1]};
+  *reinterpret_cast<u32x4*>(v_cache + dst) = u32x4{va[0], va[1], vb[0], vb[1]};
+}
+
 // ---------------------------------------------------------------------------
 // decode, pass 1: persistent waves streaming equal shares of the batch
 // ---------------------------------------------------------------------------
@@ -335,7 +399,8 @@ struct StreamArgs {
   int max_context_len;
   int64_t num_blocks;
   int num_waves;
-  int rec_rows;  // query rows per piece record
+  int rec_rows;     // query rows per piece record
+  float out_scale;  // E4M3 pools: the V scale, applied to the normalised output
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -787,16 +852,18 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfRows = 16;  // query rows per wave: the N extent of both products
 
-template <int D>
+template <int D, bool F8>
 struct MCfg {
-  static constexpr int kRow = D * 2;           // bytes per K or V token row
-  static constexpr int kNC = kRow / 16;        // 16-byte chunks per row: 8 or 16
+  static constexpr int kRowQ = D * 2;          // bytes per fp16 q row
+  static constexpr int kNCQ = kRowQ / 16;      // 16-byte chunks per q row
+  static constexpr int kRow = F8 ? D : D * 2;  // bytes per K or V token row (E4M3 or fp16)
+  static constexpr int kNC = kRow / 16;        // 16-byte chunks per K/V row: 4, 8 or 16
   static constexpr int kTK = 16;               // tokens per tile
   static constexpr int kHalf = kTK * kRow;     // bytes of K (or V) per tile
   static constexpr int kLoads = kHalf / 1024;  // 1 KB direct-to-LDS loads for each of K and V
   static constexpr int kKB = D / 32;           // products for the scores
   static constexpr int kNB = D / 16;           // products for P.V
-  static constexpr int kQ = kMfRows * kRow;      // q rows of a piece (at most 16)
+  static constexpr int kQ = kMfRows * kRowQ;     // q rows of a piece (at most 16)
   static constexpr int kStage = 2 * kHalf + kQ;  // one ring stage: K tile, V tile, q rows
   static constexpr int kRowsPerLoad = 64 / kNC;
   static_assert(kLoads * kRowsPerLoad == kTK, "a load covers whole rows");
@@ -887,6 +954,134 @@ __device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], cons
   else read_stage_d64<VM, OFF>(ka, va, k, v, e0, e1, p0, p1);
 }
 
+// ---- E4M3 pools ([CON] section 6: blocks hold compressed K/V that the kernel expands)
+//
+// A row of D codes is D bytes.  The products still run in fp16: every E4M3 value is an
+// fp16 value, so the conversion is exact, and the K and V scales are applied in fp32
+// (K's folded into the score scale, V's into the final normalisation).  Token order
+// within a tile differs from the fp16 kernel: lane quarter jq holds tokens jq, jq + 4,
+// jq + 8, jq + 12 (tau below), so that the V rows one 16-lane phase reads are adjacent.
+// V^T is built in registers: a lane reads, for each of its four tokens, the NB codes of
+// dims NB g .. NB g + NB - 1 (one 8- or 4-byte read), and a byte transpose turns them
+// into the NB operands {token 0..3} of one dim each.
+
+// Token of a tile held in score row i (the K row lane g reads is tau(g)).
+__device__ __forceinline__ int tau(int i) { return (i >> 2) + 4 * (i & 3); }
+
+// Chunk c of E4M3 row r is stored at chunk position c ^ swz8<D>(r).  The 8 lanes of one
+// ds_read_b128 cycle read rows tau(0..7) or tau(8..15) at one chunk; for D = 128 (8
+// chunks a row) swz8 takes 8 distinct values over either set, for D = 64 (4 chunks, two
+// rows per 128 bytes) 4 distinct values over its even and over its odd rows.
+template <int D>
+__device__ __forceinline__ int swz8(int r) {
+  return D == 128 ? ((r >> 2) | ((r & 1) << 2)) : ((r >> 2) & 3);
+}
+
+// Four E4M3 codes (byte i = element i) as fp16, exactly.
+__device__ __forceinline__ f16x4 e4m3x4_to_f16(uint32_t x) {
+  const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false);
+  const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true);
+  return f16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 4 x 4 byte transpose: byte j of w[i] = byte i of x[j].  v_perm_b32 picks bytes 0-3
+// from its second source and 4-7 from its first.
+__device__ __forceinline__ void byte_transpose4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                                uint32_t (&w)[4]) {
+  const uint32_t a_lo = __builtin_amdgcn_perm(x1, x0, 0x05010400u);  // x0.0 x1.0 x0.1 x1.1
+  const uint32_t a_hi = __builtin_amdgcn_perm(x1, x0, 0x07030602u);  // x0.2 x1.2 x0.3 x1.3
+  const uint32_t b_lo = __builtin_amdgcn_perm(x3, x2, 0x05010400u);
+  const uint32_t b_hi = __builtin_amdgcn_perm(x3, x2, 0x07030602u);
+  w[0] = __builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u);
+  w[1] = __builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u);
+  w[2] = __builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u);
+  w[3] = __builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u);
+}
+
+// The E4M3 stage read: like read_stage_d128, with the K codes in two ds_read_b128 and
+// the V codes of the lane's four tokens in four ds_read_b64 (D = 128), or one
+// ds_read_b128 and four ds_read_b32 (D = 64).
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_f8_d128(const uint32_t (&ka)[2], const uint32_t (&va)[4],
+                                                   u32x4 (&k)[2], u32x2 (&v)[4], const int32_t* e0,
+                                                   const int32_t* e1, int32_t& p0, int32_t& p1) {
+  asm volatile(
+      "s_load_dword %[p0], %[e0], 0x0\n\t"
+      "s_load_dword %[p1], %[e1], 0x0\n\t"
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b128 %[k1], %[ka1] offset:%[off]\n\t"
+      "ds_read_b64 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b64 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b64 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b64 %[v3], %[va3] offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]),
+        [v3] "=&v"(v[3]), [p0] "=&s"(p0), [p1] "=&s"(p1)
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]),
+        [va3] "v"(va[3]), [e0] "s"(e0), [e1] "s"(e1), [vm] "n"(VM), [off] "n"(OFF)
+      : "memory");
+}
+
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_f8_d64(const uint32_t (&ka)[1], const uint32_t (&va)[4],
+                                                  u32x4 (&k)[1], uint32_t (&v)[4], const int32_t* e0,
+                                                  const int32_t* e1, int32_t& p0, int32_t& p1) {
+  asm volatile(
+      "s_load_dword %[p0], %[e0], 0x0\n\t"
+      "s_load_dword %[p1], %[e1], 0x0\n\t"
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b32 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b32 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b32 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b32 %[v3], %[va3] offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k0] "=&v"(k[0]), [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]), [v3] "=&v"(v[3]),
+        [p0] "=&s"(p0), [p1] "=&s"(p1)
+      : [ka0] "v"(ka[0]), [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]),
+        [e0] "s"(e0), [e1] "s"(e1), [vm] "n"(VM), [off] "n"(OFF)
+      : "memory");
+}
+
+// Read an E4M3 stage and expand it into the fp16 operands of the fp16 kernel: kop[kb]
+// holds the codes of dims 8 (jq KB + kb) .. + 7 of K row tau(g); vop[nb] holds dim
+// NB g + nb of V rows tau(4 jq + t), t = 0..3.
+template <int D, int VM, int OFF>
+__device__ __forceinline__ void read_stage_f8(const uint32_t (&ka)[D / 64], const uint32_t (&va)[4],
+                                              f16x8 (&kop)[D / 32], f16x4 (&vop)[D / 16],
+                                              const int32_t* e0, const int32_t* e1, int32_t& p0,
+                                              int32_t& p1) {
+  u32x4 kr[D / 64];
+  uint32_t x[4], y[4];
+  if constexpr (D == 128) {
+    u32x2 vr[4];
+    read_stage_f8_d128<VM, OFF>(ka, va, kr, vr, e0, e1, p0, p1);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      x[t] = vr[t][0];
+      y[t] = vr[t][1];
+    }
+  } else {
+    read_stage_f8_d64<VM, OFF>(ka, va, kr, x, e0, e1, p0, p1);
+  }
+#pragma unroll
+  for (int kb = 0; kb < D / 32; ++kb) {
+    const f16x4 a = e4m3x4_to_f16(kr[kb / 2][2 * (kb % 2)]);
+    const f16x4 b = e4m3x4_to_f16(kr[kb / 2][2 * (kb % 2) + 1]);
+    kop[kb] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  }
+  uint32_t w[4];
+  byte_transpose4(x[0], x[1], x[2], x[3], w);
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) vop[nb] = e4m3x4_to_f16(w[nb]);
+  if constexpr (D == 128) {
+    byte_transpose4(y[0], y[1], y[2], y[3], w);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) vop[4 + nb] = e4m3x4_to_f16(w[nb]);
+  }
+}
+
 // Six wave-uniform 32-bit loads through the scalar unit with a single wait.
 __device__ __forceinline__ void load_entries6(const int32_t* a0, const int32_t* a1, const int32_t* a2,
                                               const int32_t* a3, const int32_t* a4, const int32_t* a5,
@@ -943,13 +1138,15 @@ __device__ __forceinline__ void unroll(F&& f) {
   unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int D, int NST>
+template <int D, int NST, bool F8>
 __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs a) {
-  using K = MCfg<D>;
+  using K = MCfg<D, F8>;
   constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
+  constexpr int ROWQ = K::kRowQ, NCQ = K::kNCQ;
   constexpr int LOADS = K::kLoads, STAGE = K::kStage, HALF = K::kHalf;
   constexpr int QOFF = 2 * HALF;             // q rows within a stage
-  constexpr int QROWS = 1024 / ROW;          // q rows per 1 KB load
+  constexpr int QROWS = 1024 / ROWQ;         // q rows per 1 KB load
+  constexpr int KR = D / 64;                 // E4M3: 16-byte K reads per lane
   constexpr int VM = (NST - 1) * 2 * LOADS;  // loads younger than a stage when it is read
   static_assert(VM <= 63, "vmcnt range");
   static_assert(NST * STAGE <= 65536, "stage offsets are 16-bit immediates");
@@ -969,30 +1166,48 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 
   // ---- per-lane LDS addresses (within a stage) of the operands, and of the loads
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
-  uint32_t ka[KB], va[NB];
+  constexpr int NKA = F8 ? KR : KB, NVA = F8 ? 4 : NB;
+  uint32_t ka[NKA], va[NVA];
+  if constexpr (F8) {
+    const int rk = tau(g);  // lane (g, jq) takes dims 8 jq KB .. 8 jq KB + 8 KB - 1 of row tau(g)
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {  // lane (g = token, jq) takes chunk jq * KB + kb of row g
-    const int c = jq * KB + kb;
-    ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz(g)) * 16));
-  }
+    for (int j = 0; j < KR; ++j)
+      ka[j] = ring + static_cast<uint32_t>(rk * ROW + (((jq * KR + j) ^ swz8<D>(rk)) * 16));
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {  // lane 16 jq + 4 i + q: row 4 jq + i, dims 16 nb + 4 q
-    const int r = 4 * jq + (g >> 2), q = g & 3;
-    const int c = 2 * nb + (q >> 1);
-    va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz(r)) * 16) + (q & 1) * 8);
+    for (int t = 0; t < 4; ++t) {  // row tau(4 jq + t) = jq + 4 t, dims NB g .. NB g + NB - 1
+      const int r = jq + 4 * t;
+      const int byte = NB * g;
+      va[t] = ring + static_cast<uint32_t>(HALF + r * ROW + (((byte >> 4) ^ swz8<D>(r)) * 16) + (byte & 15));
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {  // lane (g = token, jq) takes chunk jq * KB + kb of row g
+      const int c = jq * KB + kb;
+      ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz(g)) * 16));
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {  // lane 16 jq + 4 i + q: row 4 jq + i, dims 16 nb + 4 q
+      const int r = 4 * jq + (g >> 2), q = g & 3;
+      const int c = 2 * nb + (q >> 1);
+      va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz(r)) * 16) + (q & 1) * 8);
+    }
   }
   // q operand: lane (g, jq) reads chunks jq * KB .. jq * KB + KB - 1 of q row g
-  const uint32_t qa = ring + static_cast<uint32_t>(g * ROW + jq * KB * 16);
+  const uint32_t qa = ring + static_cast<uint32_t>(g * ROWQ + jq * KB * 16);
   // load i, lane l fills LDS position 64 i + l of a half: row r, chunk position p, which
-  // holds chunk p ^ swz(r) of the row; lo[i] is its byte offset from the row slot start
+  // holds chunk p ^ swz(r) of the row; lo[i] is its byte offset from the row slot start,
+  // hi8[i] whether the row is in the second half of the tile
   const int bsz = a.block_size;
   uint32_t lo[LOADS];
+  bool hi8[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pos = i * 64 + lane;
     const int r = pos / NC, p = pos % NC;
     const int rr = bsz >= TK ? r : (r & (bsz - 1));  // row within its block
-    lo[i] = static_cast<uint32_t>(rr * ROW + ((p ^ swz(r)) * 16));
+    const int sw = F8 ? swz8<D>(r) : swz(r);
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((p ^ sw) * 16));
+    hi8[i] = r >= 8;
   }
 
   const char* kcache = static_cast<const char*>(a.k_cache);
@@ -1049,12 +1264,12 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
       const int gtile = f.unit - kvh * a.n_gtiles;
       const int h0 = kvh * a.group + gtile * kMfRows;
       const int ng = min(kMfRows, a.group - gtile * kMfRows);
-      const char* qrow0 = qbytes + (static_cast<int64_t>(f.s) * a.num_q_heads + h0) * ROW;
+      const char* qrow0 = qbytes + (static_cast<int64_t>(f.s) * a.num_q_heads + h0) * ROWQ;
 #pragma unroll
       for (int i = 0; i < kMfRows / QROWS; ++i) {
         if (i * QROWS < ng) {
-          const int r = min(i * QROWS + lane / NC, ng - 1);
-          __builtin_amdgcn_global_load_lds(qrow0 + r * ROW + (lane % NC) * 16, stage + QOFF + i * 1024,
+          const int r = min(i * QROWS + lane / NCQ, ng - 1);
+          __builtin_amdgcn_global_load_lds(qrow0 + r * ROWQ + (lane % NCQ) * 16, stage + QOFF + i * 1024,
                                            16, 0, 0);
         }
       }
@@ -1065,7 +1280,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const bool second = bsz < TK && i * K::kRowsPerLoad >= 8;  // wave-uniform
+      // wave-uniform unless one load spans both halves (16 rows of 64 codes)
+      const bool second = bsz < TK && (K::kRowsPerLoad > 8 ? hi8[i] : i * K::kRowsPerLoad >= 8);
       const uint64_t off = (second ? b1 : b0) + lo[i];
       __builtin_amdgcn_global_load_lds(kcache + off, stage + i * 1024, 16, 0, 0);
       __builtin_amdgcn_global_load_lds(vcache + off, stage + HALF + i * 1024, 16, 0, 0);
@@ -1114,7 +1330,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      ok[i] = full || (4 * jq + i < cn);
+      ok[i] = full || ((F8 ? tau(4 * jq + i) : 4 * jq + i) < cn);
       mt = fmaxf(mt, ok[i] ? sc[i] : -INFINITY);
     }
     {  // the row maximum over the tile: lanes g, g+16, g+32, g+48
@@ -1168,19 +1384,42 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const bool whole = cc.gstart >= A && cc.gstart + cc.nt <= A_end;
     const bool head = cc.gstart < A;
     const float qnan = __builtin_nanf("");
-    const float inv = piece_bad ? qnan : 1.0f / lt;
+    const float inv = piece_bad ? qnan : (F8 ? a.out_scale / lt : 1.0f / lt);
     const int64_t row = static_cast<int64_t>(cc.s) * a.num_q_heads + h0 + g;
     const int rec = w * 2 + (head ? 0 : 1);
+    if constexpr (F8) {
+      // o[nb][r] is dim NB (4 jq + r) + nb: the lane holds dims 4 NB jq .. 4 NB jq + 4 NB - 1
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = 16 * nb + 4 * jq;
-      const f32x4 y = o[nb] * inv;
-      if (whole) {
-        const f16x4 h = {static_cast<f16>(y[0]), static_cast<f16>(y[1]), static_cast<f16>(y[2]),
-                         static_cast<f16>(y[3])};
-        *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + row * D + col) = h;
-      } else {
-        *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + g) * D + col) = y;
+      for (int r = 0; r < 4; ++r) {
+        const int col = NB * (4 * jq + r);
+        float y[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) y[nb] = o[nb][r] * inv;
+        if (whole) {
+          f16* dst = static_cast<f16*>(a.out) + row * D + col;
+#pragma unroll
+          for (int j = 0; j < NB; j += 4)
+            *reinterpret_cast<f16x4*>(dst + j) = f16x4{static_cast<f16>(y[j]), static_cast<f16>(y[j + 1]),
+                                                       static_cast<f16>(y[j + 2]), static_cast<f16>(y[j + 3])};
+        } else {
+          float* dst = a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + g) * D + col;
+#pragma unroll
+          for (int j = 0; j < NB; j += 4)
+            *reinterpret_cast<f32x4*>(dst + j) = f32x4{y[j], y[j + 1], y[j + 2], y[j + 3]};
+        }
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = 16 * nb + 4 * jq;
+        const f32x4 y = o[nb] * inv;
+        if (whole) {
+          const f16x4 h = {static_cast<f16>(y[0]), static_cast<f16>(y[1]), static_cast<f16>(y[2]),
+                           static_cast<f16>(y[3])};
+          *reinterpret_cast<f16x4*>(static_cast<f16*>(a.out) + row * D + col) = h;
+        } else {
+          *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + g) * D + col) = y;
+        }
       }
     }
     if (!whole && jq == 0) {
@@ -1237,7 +1476,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
       fbad[nxt] = fetch(cf, real, real && cf.t == 0, nxt, pe0, pe1);
       wk.advance(cf);
       entry_ptrs(cf, i + NST < n_my, e0, e1);
-      read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      if constexpr (F8) read_stage_f8<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      else read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
       if (i < n_my) process(i, stc);
     });
   }
@@ -1381,6 +1621,8 @@ struct DecodeCall {
   void* workspace;
   size_t workspace_bytes;
   hipStream_t stream;
+  bool kv_fp8 = false;  // pools hold E4M3 codes (q and out are fp16)
+  float k_scale = 1.0f, v_scale = 1.0f;
 };
 
 int check_decode(const DecodeCall& c, Geom* g) {
@@ -1411,7 +1653,7 @@ int check_decode(const DecodeCall& c, Geom* g) {
     return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles");
   if (c.num_blocks > (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "num_blocks above 2^31 - 1");
-  if (static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.dtype == PA_F16 ? 2 : 4) >
+  if (static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.kv_fp8 ? 1 : c.dtype == PA_F16 ? 2 : 4) >
       (static_cast<int64_t>(1) << 32) - 1)
     return fail(PA_ERR_INVALID_ARG, "one block of one layer exceeds 4 GiB");
   if (c.num_seqs == 0) return PA_OK;
@@ -1501,10 +1743,11 @@ int waves_valu(const DecodeCall& c, const Geom& g) {
   return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
 }
 
-template <int D>
+template <int D, bool F8>
 int waves_mfma(const DecodeCall& c, const Geom& g) {
-  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, kMfStages>));
-  int64_t base = static_cast<int64_t>(r.cus) * kMfWavesPerCU;
+  constexpr int kStages = F8 ? kF8Stages : kMfStages;
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, kStages, F8>));
+  int64_t base = static_cast<int64_t>(r.cus) * (F8 ? kF8WavesPerCU : kMfWavesPerCU);
   if (base > r.waves) base = r.waves;
   return waves_for(c, g, base);
 }
@@ -1522,7 +1765,10 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   a.v_cache = c.v_cache;
   a.block_tables = c.block_tables;
   a.context_lens = c.context_lens;
-  a.scale_log2 = static_cast<float>(static_cast<double>(c.scale) * 1.4426950408889634);
+  // E4M3 pools: the K scale multiplies every score, so it joins the softmax scale
+  a.scale_log2 = static_cast<float>(static_cast<double>(c.scale) * (c.kv_fp8 ? c.k_scale : 1.0) *
+                                    1.4426950408889634);
+  a.out_scale = c.kv_fp8 ? c.v_scale : 1.0f;
   a.block_size = c.block_size;
   a.log2_block = log2_of(c.block_size);
   a.num_kv_heads = c.num_kv_heads;
@@ -1547,11 +1793,12 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
   return check_hip("pa_stream_kernel launch");
 }
 
-template <int D>
+template <int D, bool F8>
 int launch_stream_mfma(const DecodeCall& c, const Geom& g) {
+  constexpr int kStages = F8 ? kF8Stages : kMfStages;
   StreamArgs a = stream_args(c, g);
-  a.num_waves = waves_mfma<D>(c, g);
-  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, kMfStages>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  a.num_waves = waves_mfma<D, F8>(c, g);
+  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, kStages, F8>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_mfma_kernel launch");
 }
 
@@ -1577,7 +1824,8 @@ int dispatch_f32(const DecodeCall& c, const Geom& g) {
 
 template <int Which, int D>
 int dispatch_f16(const DecodeCall& c, const Geom& g) {
-  return Which == 0 ? launch_stream_mfma<D>(c, g) : launch_reduce<f16, D, kMfRows>(c, g);
+  if (Which == 1) return launch_reduce<f16, D, kMfRows>(c, g);
+  return c.kv_fp8 ? launch_stream_mfma<D, true>(c, g) : launch_stream_mfma<D, false>(c, g);
 }
 
 // Which = 0: the stream kernel; 1: the reduce kernel
@@ -1602,6 +1850,21 @@ int launch_cache_write(const void* k, const void* v, const int64_t* slots, void*
                      num_blocks * block_size);
   return check_hip("pa_cache_write_kernel launch");
 }
+
+template <int D>
+int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, void* kc, void* vc,
+                           float k_inv, float v_inv, int num_tokens, int num_kv_heads, int block_size,
+                           int64_t num_blocks, hipStream_t stream) {
+  const int64_t chunks = static_cast<int64_t>(num_tokens) * num_kv_heads * (D / 16);
+  const int64_t blocks = (chunks + 255) / 256;
+  hipLaunchKernelGGL((pa_cache_write_fp8_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                     stream, static_cast<const f16*>(k), static_cast<const f16*>(v), slots,
+                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), k_inv, v_inv, chunks,
+                     num_kv_heads, block_size, num_blocks * block_size);
+  return check_hip("pa_cache_write_fp8_kernel launch");
+}
+
+bool valid_scale(float x) { return x > 0.0f && std::isfinite(x); }
 
 DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, float scale,
@@ -1750,6 +2013,84 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   rc = dispatch<0>(c, g);
   if (rc != PA_OK) return rc;
   return dispatch<1>(c, g);
+}
+
+int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
+                       void* v_cache, float k_scale, float v_scale, int32_t num_tokens,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                       void* stream) {
+  g_error.clear();
+  int rc = check_common(PA_F16, head_dim, block_size);
+  if (rc != PA_OK) return rc;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "k_scale %g and v_scale %g must be positive and finite",
+                static_cast<double>(k_scale), static_cast<double>(v_scale));
+  if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+  if (num_kv_heads <= 0) return fail(PA_ERR_INVALID_ARG, "num_kv_heads %d must be > 0", num_kv_heads);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks %lld must be > 0", (long long)num_blocks);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
+  // the reciprocal is rounded once, to fp32; every element is then one fp32 product
+  const float k_inv = static_cast<float>(1.0 / static_cast<double>(k_scale));
+  const float v_inv = static_cast<float>(1.0 / static_cast<double>(v_scale));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64
+             ? launch_cache_write_fp8<64>(k, v, slot_mapping, k_cache, v_cache, k_inv, v_inv, num_tokens,
+                                          num_kv_heads, block_size, num_blocks, st)
+             : launch_cache_write_fp8<128>(k, v, slot_mapping, k_cache, v_cache, k_inv, v_inv, num_tokens,
+                                           num_kv_heads, block_size, num_blocks, st);
+}
+
+static int decode_fp8(int launches, void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+                      float v_scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  DecodeCall c = make_call(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                           num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                           max_context_len, num_blocks, partition_size, PA_F16, workspace, workspace_bytes,
+                           stream);
+  c.kv_fp8 = true;
+  c.k_scale = k_scale;
+  c.v_scale = v_scale;
+  if (!valid_scale(k_scale) || !valid_scale(v_scale))
+    return fail(PA_ERR_INVALID_ARG, "k_scale %g and v_scale %g must be positive and finite",
+                static_cast<double>(k_scale), static_cast<double>(v_scale));
+  if (!valid_scale(static_cast<float>(static_cast<double>(scale) * k_scale)))
+    return fail(PA_ERR_INVALID_ARG, "scale * k_scale is not a positive finite fp32 value");
+  Geom g;
+  int rc = check_decode(c, &g);
+  if (rc != PA_OK) return rc;
+  rc = dispatch<0>(c, g);
+  if (rc != PA_OK || launches == 1) return rc;
+  return dispatch<1>(c, g);
+}
+
+int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
+                  float v_scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                  int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return decode_fp8(2, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                    block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                    max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* context_lens, float scale,
+                             float k_scale, float v_scale, int32_t block_size, int32_t num_kv_heads,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                             int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_fp8(1, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+                    block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                    max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -25,7 +25,8 @@ def _declared_functions():
 def test_header_declares_the_calls():
     names = _declared_functions()
     for want in ("pa_cache_write", "pa_decode", "pa_decode_workspace_bytes",
-                 "pa_decode_partitions", "pa_decode_reduce", "pa_last_error", "pa_abi_version"):
+                 "pa_decode_partitions", "pa_decode_reduce", "pa_last_error", "pa_abi_version",
+                 "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_fp8_partitions"):
         assert want in names
 
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16)
+    assert P.lib().pa_abi_version() == (2 << 16) | 1
 
 
 def test_workspace_size_query():
@@ -143,6 +144,78 @@ def test_reduce_rejects_bad_arguments():
     assert lib.pa_decode_reduce(FAKE, FAKE, 4, 30, 8, 128, 4096, 0, 1, FAKE, 1 << 30, None) == \
         _lib.PA_ERR_INVALID_ARG
     assert lib.pa_decode_reduce(FAKE, FAKE, 0, 32, 8, 128, 4096, 0, 1, None, 0, None) == _lib.PA_OK
+
+
+def _decode_fp8(fn="pa_decode_fp8", **over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, scale=0.1, ks=0.01, vs=0.02,
+             B=16, hkv=8, S=4, hq=32, D=128, mb=16, mcl=256, N=100, P=64, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(over)
+    return getattr(P.lib(), fn)(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["scale"],
+                                a["ks"], a["vs"], a["B"], a["hkv"], a["S"], a["hq"], a["D"], a["mb"],
+                                a["mcl"], a["N"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_fp8", "pa_decode_fp8_partitions"])
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(B=4), _lib.PA_ERR_UNSUPPORTED),
+    (dict(ks=0.0), _lib.PA_ERR_INVALID_ARG),          # scales: positive and finite
+    (dict(vs=-1.0), _lib.PA_ERR_INVALID_ARG),
+    (dict(ks=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), _lib.PA_ERR_INVALID_ARG),
+    (dict(scale=1e30, ks=1e30), _lib.PA_ERR_INVALID_ARG),  # scale * k_scale overflows fp32
+    (dict(scale=0.0), _lib.PA_ERR_INVALID_ARG),
+    (dict(hq=30), _lib.PA_ERR_INVALID_ARG),
+    (dict(mcl=257), _lib.PA_ERR_INVALID_ARG),
+    (dict(kc=FAKE + 8), _lib.PA_ERR_INVALID_ARG),
+    (dict(wsb=16), _lib.PA_ERR_WORKSPACE),
+])
+def test_decode_fp8_rejects_bad_arguments(fn, over, code):
+    assert _decode_fp8(fn, **over) == code
+    assert P.last_error() != ""
+
+
+def test_decode_fp8_with_no_sequences_is_a_no_op():
+    assert _decode_fp8(S=0, out=None, q=None) == _lib.PA_OK
+
+
+def _write_fp8(**over):
+    a = dict(k=FAKE, v=FAKE, sm=FAKE, kc=FAKE, vc=FAKE, ks=0.5, vs=0.25, T=4, hkv=8, D=128, B=16,
+             N=10, stream=None)
+    a.update(over)
+    return P.lib().pa_cache_write_fp8(a["k"], a["v"], a["sm"], a["kc"], a["vc"], a["ks"], a["vs"],
+                                      a["T"], a["hkv"], a["D"], a["B"], a["N"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=80), _lib.PA_ERR_UNSUPPORTED),
+    (dict(B=64), _lib.PA_ERR_UNSUPPORTED),
+    (dict(ks=0.0), _lib.PA_ERR_INVALID_ARG),
+    (dict(vs=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(ks=float("-inf")), _lib.PA_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(N=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(v=None), _lib.PA_ERR_INVALID_ARG),
+    (dict(vc=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
+    (dict(sm=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
+])
+def test_cache_write_fp8_rejects_bad_arguments(over, code):
+    assert _write_fp8(**over) == code
+    assert P.last_error() != ""
+
+
+def test_cache_write_fp8_with_no_tokens_is_a_no_op():
+    assert _write_fp8(T=0, k=None, v=None) == _lib.PA_OK
+
+
+def test_fp8_binding_checks_element_types():
+    import torch
+    h = torch.zeros((2, 8, 16, 128), dtype=torch.float16)
+    with pytest.raises(P.PaError, match="uint8"):
+        P.pa_decode_fp8(h, h, h, h, None, None, 0.1, 1.0, 1.0, 16, 8)
+    with pytest.raises(P.PaError, match="uint8"):
+        P.pa_cache_write_fp8(h, h, None, h, h, 1.0, 1.0)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
