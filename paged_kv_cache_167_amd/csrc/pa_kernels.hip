@@ -65,8 +65,8 @@ constexpr int kWave = 64;
 constexpr int kMaxWaves = 4096;  // persistent fp32 waves in the default split
 constexpr int kMfWavesPerCU = 4;  // persistent fp16 waves per compute unit in the default split
 constexpr int kMfStages = 3;      // LDS ring depth of the fp16 kernel
-constexpr int kF8WavesPerCU = 4;  // the same for the kernel over E4M3 pools
-constexpr int kF8Stages = 3;
+constexpr int kF8WavesPerCU = 8;  // E4M3 pools: tiles carry half the bytes, so more waves
+constexpr int kF8Stages = 2;      // with a shallower ring keep more loads in flight per CU
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -1100,6 +1100,20 @@ __device__ __forceinline__ void load_entries6(const int32_t* a0, const int32_t* 
       : "memory");
 }
 
+// Four wave-uniform 32-bit loads through the scalar unit with a single wait.
+__device__ __forceinline__ void load_entries4(const int32_t* a0, const int32_t* a1, const int32_t* a2,
+                                              const int32_t* a3, int32_t (&p)[4]) {
+  asm volatile(
+      "s_load_dword %[p0], %[a0], 0x0\n\t"
+      "s_load_dword %[p1], %[a1], 0x0\n\t"
+      "s_load_dword %[p2], %[a2], 0x0\n\t"
+      "s_load_dword %[p3], %[a3], 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [p0] "=&s"(p[0]), [p1] "=&s"(p[1]), [p2] "=&s"(p[2]), [p3] "=&s"(p[3])
+      : [a0] "s"(a0), [a1] "s"(a1), [a2] "s"(a2), [a3] "s"(a3)
+      : "memory");
+}
+
 // Read a piece's q operand from LDS: chunks kb = 0 .. KB-1 at the lane's address + OFF +
 // 16 kb.  Called after the stage wait that covers the q loads; asm for the same reason
 // as the stage reads.
@@ -1443,17 +1457,28 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   // ---- main loop, unrolled by the ring depth so that stage offsets are immediates: the
   // fetch cursor runs NST - 1 tiles ahead; every step issues the same K/V loads.  The
   // table entries of the fetch cursor's tile are always loaded one step ahead.
-  // Prologue: the cursors of the first NST tiles, and all their table entries in one
-  // batch of scalar loads (one wait instead of one per tile).
-  static_assert(NST == 3, "the prologue loads the entries of three tiles");
+  // Prologue: the cursors of the first NST tiles, and their table entries.  For rings of
+  // two and three, all the entries come in one batch of scalar loads (one wait).
   Cursor cf = cc;
-  Cursor c1 = cf;
-  wk.advance(c1);
-  Cursor c2 = c1;
-  wk.advance(c2);
   const int32_t *e0, *e1;
   int32_t pe0, pe1;
-  {
+  if constexpr (NST == 2) {
+    Cursor c1 = cf;
+    wk.advance(c1);
+    const int32_t *a0, *a1;
+    entry_ptrs(cf, true, a0, a1);
+    entry_ptrs(c1, 1 < n_my, e0, e1);
+    int32_t p[4];
+    load_entries4(uniform_ptr(a0), uniform_ptr(a1), uniform_ptr(e0), uniform_ptr(e1), p);
+    fbad[0] = fetch(cf, true, true, 0, p[0], p[1]);
+    cf = c1;
+    pe0 = p[2];
+    pe1 = p[3];
+  } else if constexpr (NST == 3) {
+    Cursor c1 = cf;
+    wk.advance(c1);
+    Cursor c2 = c1;
+    wk.advance(c2);
     const int32_t *a0, *a1, *b0, *b1;
     entry_ptrs(cf, 0 < n_my, a0, a1);
     entry_ptrs(c1, 1 < n_my, b0, b1);
@@ -1466,6 +1491,18 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     cf = c2;
     pe0 = p[4];
     pe1 = p[5];
+  } else {
+    unroll<NST - 1>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const int32_t *a0, *a1;
+      entry_ptrs(cf, j < n_my, a0, a1);
+      const int32_t p0 = scalar_load(a0), p1 = scalar_load(a1);
+      fbad[j] = fetch(cf, j < n_my, j < n_my && (j == 0 || cf.t == 0), j, p0, p1);
+      wk.advance(cf);
+    });
+    entry_ptrs(cf, NST - 1 < n_my, e0, e1);
+    pe0 = scalar_load(e0);
+    pe1 = scalar_load(e1);
   }
   for (int i0 = 0; i0 < n_my; i0 += NST) {
     unroll<NST>([&](auto stc) __attribute__((always_inline)) {
@@ -1737,17 +1774,17 @@ int waves_for(const DecodeCall& c, const Geom& g, int64_t base) {
 
 // fp32: every resident wave (at most kMaxWaves).  fp16: kMfWavesPerCU per compute unit:
 // a few deep streams per unit keep HBM busy with less contention than a full unit.
+// E4M3 pools: kF8WavesPerCU shallower streams.
 template <typename T, int D, int GT>
 int waves_valu(const DecodeCall& c, const Geom& g) {
   const Residency r = residency(reinterpret_cast<const void*>(pa_stream_kernel<T, D, GT>));
   return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
 }
 
-template <int D, bool F8>
-int waves_mfma(const DecodeCall& c, const Geom& g) {
-  constexpr int kStages = F8 ? kF8Stages : kMfStages;
-  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, kStages, F8>));
-  int64_t base = static_cast<int64_t>(r.cus) * (F8 ? kF8WavesPerCU : kMfWavesPerCU);
+template <int D, int NST, bool F8>
+int waves_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8>));
+  int64_t base = static_cast<int64_t>(r.cus) * waves_per_cu;
   if (base > r.waves) base = r.waves;
   return waves_for(c, g, base);
 }
@@ -1793,12 +1830,12 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
   return check_hip("pa_stream_kernel launch");
 }
 
-template <int D, bool F8>
-int launch_stream_mfma(const DecodeCall& c, const Geom& g) {
-  constexpr int kStages = F8 ? kF8Stages : kMfStages;
+// NST stages, waves_per_cu waves per compute unit
+template <int D, int NST, bool F8>
+int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
-  a.num_waves = waves_mfma<D, F8>(c, g);
-  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, kStages, F8>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  a.num_waves = waves_mfma<D, NST, F8>(c, g, waves_per_cu);
+  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_mfma_kernel launch");
 }
 
@@ -1825,7 +1862,8 @@ int dispatch_f32(const DecodeCall& c, const Geom& g) {
 template <int Which, int D>
 int dispatch_f16(const DecodeCall& c, const Geom& g) {
   if (Which == 1) return launch_reduce<f16, D, kMfRows>(c, g);
-  return c.kv_fp8 ? launch_stream_mfma<D, true>(c, g) : launch_stream_mfma<D, false>(c, g);
+  return c.kv_fp8 ? launch_stream_mfma<D, kF8Stages, true>(c, g, kF8WavesPerCU)
+                  : launch_stream_mfma<D, kMfStages, false>(c, g, kMfWavesPerCU);
 }
 
 // Which = 0: the stream kernel; 1: the reduce kernel
