@@ -41,7 +41,10 @@ Parity status: every function below is pinned by ``tests/test_oracle_pins.py``
 K/V, permutation / block-size / sharing invariants, closed forms); the FP8 part
 ([CON] section 6) by ``tests/test_oracle_fp8.py`` (code values fixed by the E4M3
 definition, torch's float8_e4m3fn table and rounding, brute-force nearest code,
-ties, saturation, and lossless round trips that reduce FP8 decode to the fp64 one).
+ties, saturation, and lossless round trips that reduce FP8 decode to the fp64 one);
+``prefill`` by ``tests/test_oracle_prefill.py`` (torch SDPA with a causal or bottom-right
+mask in float64, pure-Python loops, reduction to ``decode`` at one token per sequence,
+chunk-split invariance).
 """
 
 from __future__ import annotations
@@ -256,6 +259,56 @@ def decode_one_partitioned(q, k_cache, v_cache, block_tables, context_lens, scal
         num += w * o_p
         den += w
     return num / den
+
+
+# ---------------------------------------------------------------------------
+# Several query tokens per sequence: the prompt phase, in chunks, over the paged
+# cache  ([SOSP] section 2.1: the prompt is taken in at once, as matrix work;
+# [SOSP] section 5.1, item 5 and [VATT] "3 分钟速读" point 1: paged prefill,
+# later done in chunks).  Reading: the chunk's n tokens are the last n positions
+# of the context (written before attention, as a decode step writes its token:
+# [SOSP] section 3.4), and query i, at position ctx - n + i, attends causally to
+# positions 0 .. ctx - n + i.  n = 1 is the decode step.
+# ---------------------------------------------------------------------------
+
+def visible_keys(ctx: int, n: int, i: int) -> int:
+    """Keys that query i of an n-token chunk ending a ctx-token context sees: positions
+    0 .. ctx - n + i, its own included."""
+    return ctx - n + i + 1
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float,
+            block_size: int, num_kv_heads: int) -> np.ndarray:
+    """Outputs of every query token, float64 [total_q, Hq, D].
+
+    q:            [total_q, Hq, D]; sequence s owns rows query_start[s] .. query_start[s+1]-1
+    query_start:  [S + 1] non-decreasing offsets, query_start[0] = 0
+    context_lens: [S], counting the chunk; a chunk longer than its context is
+                  invalid and gives NaN rows.
+    For each row: softmax(scale * K[:p+1] q_row) V[:p+1] with p the row's position.
+    """
+    total_q, num_q_heads, d = q.shape
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((total_q, num_q_heads, d), dtype=np.float64)
+    for s in range(len(context_lens)):
+        r0, r1 = int(query_start[s]), int(query_start[s + 1])
+        n, ctx = r1 - r0, int(context_lens[s])
+        if n == 0:
+            continue
+        if n > ctx:
+            out[r0:r1] = np.nan
+            continue
+        for kvh in range(num_kv_heads):
+            keys = gather_head(k_cache, block_tables[s], ctx, block_size, kvh)
+            vals = gather_head(v_cache, block_tables[s], ctx, block_size, kvh)
+            for i in range(n):
+                m = visible_keys(ctx, n, i)
+                for g in range(group):
+                    h = kvh * group + g
+                    qv = np.asarray(q[r0 + i, h], dtype=np.float64)
+                    p = softmax(float(scale) * (keys[:m] @ qv))
+                    out[r0 + i, h] = p @ vals[:m]
+    return out
 
 
 # ---------------------------------------------------------------------------

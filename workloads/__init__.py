@@ -35,6 +35,11 @@ __all__ = [
     "shared_prefix",
     "long_context",
     "CONFIGS",
+    "PagedPrefillCase",
+    "make_prefill_case",
+    "prefill_llama3_8b",
+    "prefill_llama2_70b",
+    "PREFILL_CONFIGS",
 ]
 
 
@@ -458,4 +463,168 @@ CONFIGS = {
     "llama2_70b": llama2_70b,
     "shared_prefix": shared_prefix,
     "long_context": long_context,
+}
+
+
+# ---------------------------------------------------------------------------
+# several query tokens per sequence (a prompt chunk)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class PagedPrefillCase:
+    """One chunked-prefill step's inputs.  Shapes:
+
+    q            [Tq, Hq, D]          the chunk's queries, sequences one after another
+    query_start  [S + 1]              int32 offsets of each sequence's rows in q
+    context_lens [S]                  int32, counting the chunk (its tokens are the last ones)
+    block_tables [S, max_blocks]      int32, -1 past each sequence's last block
+    prefix_k/v   [Tp, Hkv, D]         the tokens before each chunk, already stored
+    prefix_slots [Tp]                 int64
+    new_k/v      [Tq, Hkv, D]         the chunk's own K/V, written in the step
+    new_slots    [Tq]                 int64
+    """
+
+    name: str
+    dtype: np.dtype
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    context_lens: np.ndarray
+    query_start: np.ndarray
+    block_tables: np.ndarray
+    q: np.ndarray
+    prefix_k: np.ndarray
+    prefix_v: np.ndarray
+    prefix_slots: np.ndarray
+    new_k: np.ndarray
+    new_v: np.ndarray
+    new_slots: np.ndarray
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def query_lens(self) -> np.ndarray:
+        return np.diff(self.query_start).astype(np.int64)
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max()) if self.num_seqs else 0
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def elt_bytes(self) -> int:
+        return int(np.dtype(self.dtype).itemsize)
+
+    def empty_pool(self) -> np.ndarray:
+        return np.full((self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim),
+                       np.nan, dtype=self.dtype)
+
+    def flops(self) -> int:
+        """Causal attention work: 4 D flops per (query head, query token, visible key)."""
+        n = self.query_lens
+        c = self.context_lens.astype(np.int64)
+        # keys visible to the chunk's rows: sum over i < n of (c - n + i + 1)
+        visible = n * (c - n) + n * (n + 1) // 2
+        return int(4 * self.head_dim * self.num_q_heads * visible.sum())
+
+    def kv_bytes(self) -> int:
+        """K+V bytes of every context, read once."""
+        return int(self.context_lens.astype(np.int64).sum()) * self.num_kv_heads * \
+            self.head_dim * 2 * self.elt_bytes
+
+
+def make_prefill_case(*, name="custom_prefill", seed=0, dtype=np.float16, context_lens, query_lens,
+                      num_q_heads, num_kv_heads, head_dim, block_size, pool_factor=1.2,
+                      num_blocks=None, sigma=0.5, scale=None, variant="plain",
+                      logical_seed=None, extra_table_cols=0) -> PagedPrefillCase:
+    """Each sequence holds ctx tokens, the last n of which are the chunk being prefilled.
+
+    K/V come from the same per-sequence streams as make_case (so a logical seed fixes them
+    independently of the block size); the chunk's queries from their own streams.
+    Variants: "plain", or "poscode" (coordinate 0 of V is position / max ctx).
+    """
+    assert num_q_heads % num_kv_heads == 0
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    qlen = np.asarray(query_lens, dtype=np.int64)
+    if ctx.shape != qlen.shape or np.any(qlen < 0) or np.any(qlen > ctx):
+        raise ValueError("need 0 <= query_lens <= context_lens, one per sequence")
+    if variant not in ("plain", "poscode"):
+        raise ValueError(f"unknown prefill variant {variant!r}")
+    if scale is None:
+        scale = 1.0 / np.sqrt(head_dim)
+    lseed = seed if logical_seed is None else logical_seed
+    blocks_per_seq = [int(-(-c // block_size)) for c in ctx]
+    if num_blocks is None:
+        num_blocks = max(1, int(np.ceil(pool_factor * max(sum(blocks_per_seq), 1))))
+    alloc = BlockAllocator(num_blocks, np.random.default_rng([seed, 7, block_size]))
+    width = (max(blocks_per_seq) if blocks_per_seq else 1) + extra_table_cols
+    tables = _tables_from(alloc, blocks_per_seq, width)
+    _, logical = _logical_data(lseed, np.maximum(ctx, 1), num_q_heads, num_kv_heads, head_dim,
+                               sigma, dtype, variant)
+    pk, pv, ps, nk, nv, ns, qs = [], [], [], [], [], [], []
+    for s, c in enumerate(ctx):
+        c, n = int(c), int(qlen[s])
+        k, v = logical[s]
+        k, v = k[:c], v[:c]
+        slots = _slots(tables[s], np.arange(c), block_size)
+        pk.append(k[:c - n])
+        pv.append(v[:c - n])
+        ps.append(slots[:c - n])
+        nk.append(k[c - n:])
+        nv.append(v[c - n:])
+        ns.append(slots[c - n:])
+        qs.append(_normal(np.random.default_rng([lseed, 10, s]), (n, num_q_heads, head_dim), sigma,
+                          dtype))
+    cat = lambda xs, shape: np.concatenate(xs, axis=0) if xs else np.zeros(shape, dtype)  # noqa: E731
+    d = head_dim
+    return PagedPrefillCase(
+        name=name, dtype=np.dtype(dtype), num_seqs=len(ctx), num_q_heads=num_q_heads,
+        num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+        num_blocks=int(num_blocks), scale=float(scale), context_lens=ctx.astype(np.int32),
+        query_start=np.concatenate([[0], np.cumsum(qlen)]).astype(np.int32),
+        block_tables=tables, q=cat(qs, (0, num_q_heads, d)),
+        prefix_k=cat(pk, (0, num_kv_heads, d)), prefix_v=cat(pv, (0, num_kv_heads, d)),
+        prefix_slots=np.concatenate(ps).astype(np.int64) if ps else np.zeros(0, np.int64),
+        new_k=cat(nk, (0, num_kv_heads, d)), new_v=cat(nv, (0, num_kv_heads, d)),
+        new_slots=np.concatenate(ns).astype(np.int64) if ns else np.zeros(0, np.int64),
+        meta={"variant": variant, "seed": seed, "sigma": sigma})
+
+
+def prefill_llama3_8b(variant="plain", num_seqs=8, chunk=512) -> PagedPrefillCase:
+    """Chunked prefill: 8 sequences, each with U[1024, 3584] tokens already cached and a
+    512-token chunk; 32 q / 8 kv heads, D 128, B 16, pool 1.2x, fp16."""
+    rng = np.random.default_rng(1006)
+    prior = rng.integers(1024, 3584, size=num_seqs, endpoint=True)
+    return make_prefill_case(name="prefill_llama3_8b", seed=1006, dtype=np.float16,
+                             context_lens=prior + chunk, query_lens=[chunk] * num_seqs,
+                             num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                             sigma=0.5, variant=variant)
+
+
+def prefill_llama2_70b(variant="plain", num_seqs=4, prompt=2048) -> PagedPrefillCase:
+    """Whole prompts: 4 sequences of 2048 tokens prefilled at once (ctx = n = 2048);
+    64 q / 8 kv heads, D 128, B 16, pool 1.2x, fp16."""
+    return make_prefill_case(name="prefill_llama2_70b", seed=1007, dtype=np.float16,
+                             context_lens=[prompt] * num_seqs, query_lens=[prompt] * num_seqs,
+                             num_q_heads=64, num_kv_heads=8, head_dim=128, block_size=16,
+                             sigma=0.5, variant=variant)
+
+
+PREFILL_CONFIGS = {
+    "prefill_llama3_8b": prefill_llama3_8b,
+    "prefill_llama2_70b": prefill_llama2_70b,
 }
