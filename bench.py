@@ -61,7 +61,9 @@ def parse():
 
 ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
                "long_context_b16", "long_context_b32", "llama3_8b_fp8", "llama2_70b_fp8",
-               "long_context_b16_fp8"]
+               "long_context_b16_fp8", "prefill_llama3_8b", "prefill_llama2_70b"]
+PREFILL = ("prefill_llama3_8b", "prefill_llama2_70b")
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, published
 WORKLOAD_NAMES = {
     "tiny_fp32": "tiny fp32 decode (4 sequences, ctx 1..250)",
     "llama3_8b": "Llama-3-8B-shaped decode layer",
@@ -73,6 +75,8 @@ WORKLOAD_NAMES = {
     "llama3_8b_fp8": "Llama-3-8B-shaped decode layer, FP8 E4M3 KV cache",
     "llama2_70b_fp8": "Llama-2-70B-shaped 8K-context decode layer, FP8 E4M3 KV cache",
     "long_context_b16_fp8": "32K-128K context decode, block size 16, FP8 E4M3 KV cache",
+    "prefill_llama3_8b": "chunked prefill, Llama-3-8B shape: 8 x 512-token chunks after 1K-3.5K cached tokens",
+    "prefill_llama2_70b": "whole-prompt prefill, Llama-2-70B shape: 4 prompts of 2048 tokens",
 }
 FP8_SUFFIX = "_fp8"
 
@@ -171,7 +175,7 @@ def main():
     import workloads
     workloads.set_progress(log)
     for name in (ALL_CONFIGS if args.config == "all" else [args.config]):
-        result = run_one(args, name)
+        result = run_prefill(args, name) if name in PREFILL else run_one(args, name)
         print(json.dumps(result), flush=True)
         torch.cuda.empty_cache()
 
@@ -377,6 +381,116 @@ def run_one(args, config):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, fp8)
     del k_cache, v_cache, ws
+    return result
+
+
+def prefill_cpu_baseline(case):
+    """The oracle on one sequence's chunk (about 10 s of CPU work at most), scaled to flops."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import pa_oracle as O
+    kc, vc = O.cache_write(case.prefix_k, case.prefix_v, case.prefix_slots, case.empty_pool(),
+                           case.empty_pool(), case.block_size)
+    kc, vc = O.cache_write(case.new_k, case.new_v, case.new_slots, kc, vc, case.block_size)
+    n_all = int(case.query_start[1])
+    ctx = int(case.context_lens[0])
+    n = n_all
+    with threadpool_limits(limits=1):
+        while True:  # a prefix of sequence 0's chunk: rows 0 .. n-1 (the context cut after them)
+            t0 = time.perf_counter()
+            O.prefill(case.q[:n], kc, vc, case.block_tables[:1],
+                      np.array([ctx - n_all + n], np.int32), np.array([0, n], np.int32),
+                      case.scale, case.block_size, case.num_kv_heads)
+            dt = time.perf_counter() - t0
+            if dt < 30.0 or n <= 8:
+                break
+            n = max(8, int(n * 20.0 / dt))
+    c0 = ctx - n_all  # cached tokens before the chunk
+    flops = 4 * case.head_dim * case.num_q_heads * (n * c0 + n * (n + 1) // 2)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "seconds": dt, "sample": f"the first {n} of sequence 0's {n_all} chunk tokens "
+                                     "(one call), numpy float64, BLAS limited to 1 thread"}
+
+
+def run_prefill(args, config):
+    """One step = pa_cache_write of every chunk token, then pa_prefill; TFLOP/s of attention."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_167_amd as P
+    import workloads as W
+    dev = torch.device("cuda:0")
+    log(f"generating workload {config}")
+    case = W.PREFILL_CONFIGS[config]()
+    flops = case.flops()
+    log(f"  {case.num_seqs} seqs, {case.total_q} query tokens, {flops / 1e9:.1f} GFLOP per step")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q, tables, ctx, qs = t(case.q), t(case.block_tables), t(case.context_lens), t(case.query_start)
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    k_cache = torch.full(shape, float("nan"), dtype=torch.float16, device=dev)
+    v_cache = torch.full(shape, float("nan"), dtype=torch.float16, device=dev)
+    if len(case.prefix_slots):
+        P.pa_cache_write(t(case.prefix_k), t(case.prefix_v), t(case.prefix_slots), k_cache, v_cache)
+    new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    mql, mcl = case.max_query_len, case.max_context_len
+
+    def write_only():
+        P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
+
+    def prefill_only():
+        P.pa_prefill(out, q, k_cache, v_cache, tables, ctx, qs, case.scale, case.block_size,
+                     case.num_kv_heads, mql, max_context_len=mcl, stream=stream)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        write_only()
+        prefill_only()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        write_only()
+        prefill_only()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    per = {}
+    for key, fn in (("prefill", prefill_only), ("write", write_only)):
+        fn()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per[key] = e0.elapsed_time(e1) / args.steps
+    achieved = flops / (per["prefill"] * 1e-3) / 1e12
+    kv = case.kv_bytes()
+    result = {
+        "metric": "chunked-prefill attention TFLOP/s over the paged cache",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[config], "name": config, "num_seqs": case.num_seqs,
+                   "num_q_heads": case.num_q_heads, "num_kv_heads": case.num_kv_heads,
+                   "head_dim": case.head_dim, "block_size": case.block_size,
+                   "query_tokens": case.total_q,
+                   "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}",
+                   "flops_per_step": flops, "kv_bytes": kv},
+        "pa_prefill": {"us": round(per["prefill"] * 1e3, 2), "tflops": round(achieved, 2),
+                       "query_tokens_per_s": round(case.total_q / (per["prefill"] * 1e-3), 1)},
+        "pa_cache_write": {"us": round(per["write"] * 1e3, 2)},
+        "roofline": {"kernel": "pa_prefill_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "alg_flops_per_launch": flops, "avg_launch_us": round(per["prefill"] * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = prefill_cpu_baseline(case)
     return result
 
 

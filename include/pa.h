@@ -211,12 +211,47 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
                              int64_t num_blocks, int32_t partition_size,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_prefill -- causal attention of several query tokens per sequence (a prompt chunk)
+ * over the paged cache: the prompt phase of [SOSP] section 2.1, taken in chunks as in
+ * [SOSP] section 5.1 (item 5); [VATT] "3 分钟速读" point 1 measures such paged prefill
+ * kernels.
+ *
+ * Sequence s owns query rows query_start[s] .. query_start[s+1] - 1, n of them.  They are
+ * the last n positions of its context_lens[s] = ctx tokens, whose K/V must already be in
+ * the pools (pa_cache_write of the chunk first, as a decode step writes its token).  Row
+ * i, at position p = ctx - n + i, and query head h (kv head h / G):
+ *   out[row, h, :] = softmax(scale * K_s[0..p] q[row, h]) V_s[0..p]
+ * so each token sees the cached prefix and the chunk up to itself.  n = 1 is a decode step.
+ * Arithmetic: fp16 products on the matrix cores with fp32 accumulation, fp32 softmax;
+ * probabilities are rounded to fp16 for P.V as in pa_decode.
+ *
+ * q, out             device, [total_q, num_q_heads, head_dim] fp16 (total_q = query_start[num_seqs])
+ * k_cache, v_cache   device, [num_blocks, num_kv_heads, block_size, head_dim] fp16
+ * block_tables       device, [num_seqs, max_blocks_per_seq] int32
+ * context_lens       device, [num_seqs] int32, counting the chunk
+ * query_start        device, [num_seqs + 1] int32, non-decreasing, query_start[0] = 0
+ * max_query_len      host bound on every n; max_context_len: host bound on every ctx
+ * dtype              PA_F16 (PA_F32 is not built for this call)
+ * Device-side checks: a sequence with n > ctx, ctx > max_context_len or n > max_query_len
+ * gets NaN rows (only rows below max_query_len are ever written); a table entry outside
+ * [0, num_blocks) within the keys a work-group reads is not dereferenced and that
+ * work-group's rows get NaN.  No workspace; rows of different sequences never interact.
+ * returns PA_OK, or a negative code with nothing launched.
+ */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+               float scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+               int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+               int32_t max_query_len, int32_t max_context_len, int64_t num_blocks, int32_t dtype,
+               void* stream);
+
 /* Description of the last error on the calling thread ("" if none); valid until the next call. */
 const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 1)
+#define PA_ABI_VERSION ((2 << 16) | 2)
 
 #ifdef __cplusplus
 }

@@ -18,4 +18,5 @@ from ._lib import (  # noqa: F401
     pa_decode_partitions,
     pa_decode_reduce,
     pa_decode_workspace_bytes,
+    pa_prefill,
 )

@@ -52,6 +52,9 @@ SIGNATURES = {
                                             ctypes.c_float, ctypes.c_float, _c_int32, _c_int32,
                                             _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                             _c_int64, _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_prefill": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
+                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64,
+                              _c_int32, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_c_int32, []),
 }
@@ -240,3 +243,20 @@ def pa_decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_len
                                        partition_size, workspace, stream)
     _check("pa_decode_fp8_partitions", lib().pa_decode_fp8_partitions(*args))
     return workspace
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start, scale,
+               block_size, num_kv_heads, max_query_len, max_context_len=None, stream=None):
+    """Causal attention of each sequence's chunk of query tokens (rows query_start[s] ..
+    query_start[s+1]-1, the last positions of its context) over the paged cache."""
+    total_q, num_q_heads, head_dim = q.shape
+    num_seqs = context_lens.shape[0]
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    code = lib().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        _ptr(query_start), float(scale), int(block_size), int(num_kv_heads), num_seqs, num_q_heads,
+        head_dim, max_blocks, int(max_query_len), int(max_context_len), k_cache.shape[0],
+        _dtype_code(q), _stream(q, stream))
+    _check("pa_prefill", code)

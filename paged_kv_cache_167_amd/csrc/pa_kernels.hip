@@ -107,6 +107,11 @@ __device__ __forceinline__ int wave_incl_scan_int(int x, int lane) {
   return x;
 }
 
+__device__ __forceinline__ int wave_min_int(int x) {
+  for (int o = kWave / 2; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
   for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
   return x;
@@ -1100,6 +1105,17 @@ __device__ __forceinline__ void load_entries6(const int32_t* a0, const int32_t* 
       : "memory");
 }
 
+// Two wave-uniform 32-bit loads through the scalar unit with a single wait.
+__device__ __forceinline__ void load_entries2(const int32_t* a0, const int32_t* a1, int32_t (&p)[2]) {
+  asm volatile(
+      "s_load_dword %[p0], %[a0], 0x0\n\t"
+      "s_load_dword %[p1], %[a1], 0x0\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [p0] "=&s"(p[0]), [p1] "=&s"(p[1])
+      : [a0] "s"(a0), [a1] "s"(a1)
+      : "memory");
+}
+
 // Four wave-uniform 32-bit loads through the scalar unit with a single wait.
 __device__ __forceinline__ void load_entries4(const int32_t* a0, const int32_t* a1, const int32_t* a2,
                                               const int32_t* a3, int32_t (&p)[4]) {
@@ -1522,6 +1538,401 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 }
 
 // ---------------------------------------------------------------------------
+// Several query tokens per sequence: causal attention of a prompt chunk over the paged
+// cache.  Sequence s has n = query_start[s+1] - query_start[s] query tokens, the last n
+// positions of its context; query i (position ctx - n + i) sees positions 0 .. ctx - n + i.
+//
+// One work-group of four waves per (query-row block, kv head, sequence).  The rows of a
+// (sequence, kv head) are its chunk tokens times the G query heads of the group, token
+// major; a work-group takes 256 of them (64 per wave, four 16-row product blocks), so
+// every K/V tile it brings into LDS serves 256 rows.  The tiles hold 32 keys and pass
+// through a 3-stage ring that the four waves fill together (each loads 8 key rows, which
+// lie in one block for block sizes 8, 16 and 32) and read after a barrier.  Per tile and
+// 16-row block: scores S^T = K Q^T with two 16x16x32 products per 32 dims (one per key
+// half), and O^T += V^T P^T with one 16x16x32 product per 16 dims, its 32 keys in the
+// order {4j..4j+3, 16+4j..16+4j+3} of lane quarter j, which is where the two score halves
+// leave them; V^T comes from two transposing reads.  Rows past the chunk, keys past a
+// row's position and keys past the context are masked; the mask is built only for tiles
+// that cross one of those limits.
+// ---------------------------------------------------------------------------
+
+constexpr int kPfWaves = 4;                            // waves per work-group
+constexpr int kPfBlocks = 4;                           // 16-row product blocks per wave
+constexpr int kPfRows = kPfWaves * kPfBlocks * 16;     // query rows per work-group
+constexpr int kPfKeys = 32;                            // keys per tile
+constexpr int kPfStages = 3;
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* query_start;
+  float scale_log2;
+  int block_size;
+  int log2_block;
+  int num_kv_heads;
+  int num_q_heads;
+  int group;
+  int max_blocks_per_seq;
+  int max_query_len;
+  int max_context_len;
+  int64_t num_blocks;
+  int n_row_blocks;  // work-groups per (sequence, kv head)
+};
+
+template <int D>
+struct PCfg {
+  static constexpr int kRow = D * 2;                      // bytes per fp16 row
+  static constexpr int kNC = kRow / 16;                   // 16-byte chunks per row
+  static constexpr int kTile = kPfKeys * kRow;            // bytes of K (or V) per tile
+  static constexpr int kStage = 2 * kTile;
+  static constexpr int kWaveRows = kPfKeys / kPfWaves;    // key rows each wave loads
+  static constexpr int kLoads = kWaveRows * kRow / 1024;  // 1 KB loads per wave for each of K, V
+  static constexpr int kKB = D / 32;
+  static constexpr int kNB = D / 16;
+  static_assert(kLoads * 1024 == kWaveRows * kRow, "a wave loads whole rows");
+};
+
+// Stage read of the prefill ring, D = 128: issue the scalar load of the next table entry,
+// wait for this wave's loads of the stage, meet the other waves at the barrier (their
+// loads have landed and none still reads the stage to be refilled next), then read the K
+// operands of both key halves (the second half is 16 rows further) and the V^T operands.
+template <int VM, int OFF, int ROW>
+__device__ __forceinline__ void pf_read_d128(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                             f16x8 (&k)[2][4], f16x4 (&v)[2][8], const int32_t* e,
+                                             int32_t& p) {
+  asm volatile(
+      "s_load_dword %[p], %[e], 0x0\n\t"
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "s_barrier\n\t"
+      "ds_read_b128 %[k00], %[ka0] offset:%[o0]\n\t"
+      "ds_read_b128 %[k01], %[ka1] offset:%[o0]\n\t"
+      "ds_read_b128 %[k02], %[ka2] offset:%[o0]\n\t"
+      "ds_read_b128 %[k03], %[ka3] offset:%[o0]\n\t"
+      "ds_read_b128 %[k10], %[ka0] offset:%[o1]\n\t"
+      "ds_read_b128 %[k11], %[ka1] offset:%[o1]\n\t"
+      "ds_read_b128 %[k12], %[ka2] offset:%[o1]\n\t"
+      "ds_read_b128 %[k13], %[ka3] offset:%[o1]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k00] "=&v"(k[0][0]), [k01] "=&v"(k[0][1]), [k02] "=&v"(k[0][2]), [k03] "=&v"(k[0][3]),
+        [k10] "=&v"(k[1][0]), [k11] "=&v"(k[1][1]), [k12] "=&v"(k[1][2]), [k13] "=&v"(k[1][3]),
+        [p] "=&s"(p)
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [e] "s"(e),
+        [vm] "n"(VM), [o0] "n"(OFF), [o1] "n"(OFF + 16 * ROW)
+      : "memory");
+  asm volatile(
+      "ds_read_b64_tr_b16 %[v00], %[va0] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v01], %[va1] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v02], %[va2] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v03], %[va3] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v04], %[va4] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v05], %[va5] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v06], %[va6] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v07], %[va7] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v10], %[va0] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v11], %[va1] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v12], %[va2] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v13], %[va3] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v14], %[va4] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v15], %[va5] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v16], %[va6] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v17], %[va7] offset:%[o1]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [v00] "=&v"(v[0][0]), [v01] "=&v"(v[0][1]), [v02] "=&v"(v[0][2]), [v03] "=&v"(v[0][3]),
+        [v04] "=&v"(v[0][4]), [v05] "=&v"(v[0][5]), [v06] "=&v"(v[0][6]), [v07] "=&v"(v[0][7]),
+        [v10] "=&v"(v[1][0]), [v11] "=&v"(v[1][1]), [v12] "=&v"(v[1][2]), [v13] "=&v"(v[1][3]),
+        [v14] "=&v"(v[1][4]), [v15] "=&v"(v[1][5]), [v16] "=&v"(v[1][6]), [v17] "=&v"(v[1][7])
+      : [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),
+        [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [o0] "n"(OFF), [o1] "n"(OFF + 16 * ROW)
+      : "memory");
+}
+
+template <int VM, int OFF, int ROW>
+__device__ __forceinline__ void pf_read_d64(const uint32_t (&ka)[2], const uint32_t (&va)[4],
+                                            f16x8 (&k)[2][2], f16x4 (&v)[2][4], const int32_t* e,
+                                            int32_t& p) {
+  asm volatile(
+      "s_load_dword %[p], %[e], 0x0\n\t"
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "s_barrier\n\t"
+      "ds_read_b128 %[k00], %[ka0] offset:%[o0]\n\t"
+      "ds_read_b128 %[k01], %[ka1] offset:%[o0]\n\t"
+      "ds_read_b128 %[k10], %[ka0] offset:%[o1]\n\t"
+      "ds_read_b128 %[k11], %[ka1] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v00], %[va0] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v01], %[va1] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v02], %[va2] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v03], %[va3] offset:%[o0]\n\t"
+      "ds_read_b64_tr_b16 %[v10], %[va0] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v11], %[va1] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v12], %[va2] offset:%[o1]\n\t"
+      "ds_read_b64_tr_b16 %[v13], %[va3] offset:%[o1]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k00] "=&v"(k[0][0]), [k01] "=&v"(k[0][1]), [k10] "=&v"(k[1][0]), [k11] "=&v"(k[1][1]),
+        [v00] "=&v"(v[0][0]), [v01] "=&v"(v[0][1]), [v02] "=&v"(v[0][2]), [v03] "=&v"(v[0][3]),
+        [v10] "=&v"(v[1][0]), [v11] "=&v"(v[1][1]), [v12] "=&v"(v[1][2]), [v13] "=&v"(v[1][3]),
+        [p] "=&s"(p)
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]),
+        [va3] "v"(va[3]), [e] "s"(e), [vm] "n"(VM), [o0] "n"(OFF), [o1] "n"(OFF + 16 * ROW)
+      : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const PrefillArgs a) {
+  using C = PCfg<D>;
+  constexpr int ROW = C::kRow, NC = C::kNC, TILE = C::kTile, STAGE = C::kStage;
+  constexpr int LOADS = C::kLoads, KB = C::kKB, NB = C::kNB, NR = kPfBlocks, NST = kPfStages;
+  constexpr int VM = (NST - 2) * 2 * LOADS;  // loads younger than the stage being read
+  static_assert(NST * STAGE + 16 * ROW <= 65536, "LDS offsets are 16-bit immediates");
+  __shared__ __align__(1024) char s_ring[NST * STAGE];
+  __shared__ int s_bad;
+
+  const int w = threadIdx.x / kWave;  // wave in the work-group
+  const int lane = threadIdx.x % kWave;
+  const int g = lane % 16, jq = lane / 16;
+  const int rb = a.n_row_blocks - 1 - static_cast<int>(blockIdx.x);  // longest blocks first
+  const int kvh = blockIdx.y;
+  const int s = blockIdx.z;
+  const int G = a.group;
+
+  // every value below is uniform over the work-group
+  const int r0 = a.query_start[s];
+  const int n = a.query_start[s + 1] - r0;
+  const int ctx = a.context_lens[s];
+  const int row_lo = rb * kPfRows;  // first row (token-major: token * G + head)
+  if (n <= 0 || row_lo >= n * G) return;
+  const int row_hi = min(n * G, row_lo + kPfRows);  // one past the last row
+  const int t_last = (row_hi - 1) / G;
+  f16* out = static_cast<f16*>(a.out);
+  const int64_t hq = a.num_q_heads;
+  auto out_row = [&](int t, int hg) { return out + ((static_cast<int64_t>(r0) + t) * hq + kvh * G + hg) * D; };
+
+  if (n > ctx || ctx > a.max_context_len || n > a.max_query_len) {  // invalid: NaN rows
+    for (int r = row_lo + static_cast<int>(threadIdx.x) / (D / 8); r < row_hi; r += kPfWaves * kWave / (D / 8))
+      *reinterpret_cast<u32x4*>(out_row(r / G, r % G) + (threadIdx.x % (D / 8)) * 8) =
+          u32x4{0x7E007E00u, 0x7E007E00u, 0x7E007E00u, 0x7E007E00u};
+    return;
+  }
+  const int kend = ctx - n + t_last + 1;  // keys the work-group needs: 0 .. kend - 1 (<= ctx)
+  const int T = (kend + kPfKeys - 1) / kPfKeys;
+
+  // ---- query rows of this lane: row 64 w + 16 nr + g of the block; its position limit
+  int lim[NR];
+  bool rvalid[NR];
+  f16x8 qop[NR][KB];
+  int wave_min_lim = 0x7FFFFFFF;
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    const int r = row_lo + 64 * w + 16 * nr + g;
+    rvalid[nr] = r < row_hi;
+    const int t = r / G;
+    lim[nr] = rvalid[nr] ? ctx - n + t : kend - 1;  // last key the row sees
+    const f16* qr = static_cast<const f16*>(a.q) + ((static_cast<int64_t>(r0) + t) * hq + kvh * G + r % G) * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+      qop[nr][kb] = rvalid[nr] ? *reinterpret_cast<const f16x8*>(qr + (jq * KB + kb) * 8) : f16x8{};
+  }
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) wave_min_lim = min(wave_min_lim, lim[nr]);
+  wave_min_lim = wave_min_int(wave_min_lim);
+
+  // ---- LDS addresses of the operands (first key half; the second is 16 rows further)
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
+  uint32_t ka[KB], va[NB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+    ka[kb] = ring + static_cast<uint32_t>(g * ROW + (((jq * KB + kb) ^ swz(g)) * 16));
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = 4 * jq + (g >> 2), qq = g & 3;
+    const int c = 2 * nb + (qq >> 1);
+    va[nb] = ring + static_cast<uint32_t>(TILE + r * ROW + ((c ^ swz(r)) * 16) + (qq & 1) * 8);
+  }
+  // loads: wave w brings key rows 8 w .. 8 w + 7 of each tile; load i, lane l fills LDS
+  // position 64 i + l of that run (row rr, chunk position p, holding chunk p ^ swz(row))
+  uint32_t lo[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = i * 64 + lane;
+    const int rr = pos / NC, pp = pos % NC;
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((pp ^ swz((C::kWaveRows * w + rr) & 15)) * 16));
+  }
+  const int bsz = a.block_size;
+  const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
+  const uint64_t block_bytes = head_bytes * static_cast<uint64_t>(a.num_kv_heads);
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+  const int32_t* trow = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq;
+
+  // table entry of this wave's rows in tile f (a valid address for phantom tiles)
+  auto entry_ptr = [&](int f) __attribute__((always_inline)) -> const int32_t* {
+    const int key0 = f * kPfKeys + C::kWaveRows * w;
+    return uniform_ptr(key0 < kend ? trow + (key0 >> a.log2_block) : a.block_tables);
+  };
+  bool bad = false;
+  auto fetch = [&](int f, int st, int p) __attribute__((always_inline)) {
+    const int key0 = f * kPfKeys + C::kWaveRows * w;
+    const bool real = key0 < kend;  // phantom tiles and rows past the context read block 0
+    if (real && (p < 0 || p >= a.num_blocks)) {
+      bad = true;
+      p = 0;
+    }
+    if (!real) p = 0;
+    const uint64_t base = static_cast<uint64_t>(static_cast<uint32_t>(p)) * block_bytes +
+                          static_cast<uint64_t>(kvh) * head_bytes +
+                          static_cast<uint64_t>(real ? (key0 & (bsz - 1)) : 0) * ROW;
+    char* dst = s_ring + st * STAGE + C::kWaveRows * w * ROW;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      // (explicit casts: without them the host pass of this compiler drops the kernel)
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kcache + base + lo[i]),
+                                       static_cast<void*>(dst + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vcache + base + lo[i]),
+                                       static_cast<void*>(dst + TILE + i * 1024), 16, 0, 0);
+    }
+  };
+
+  // ---- softmax state and accumulators
+  f32x4 o[NR][NB];
+  float m[NR], l[NR];
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    m[nr] = -INFINITY;
+    l[nr] = 0.0f;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nr][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+
+  auto consume = [&](int f, const f16x8 (&kop)[2][KB], f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
+    constexpr float kRebase = 8.0f;
+    const int key_base = f * kPfKeys;
+    const bool causal_free = key_base + kPfKeys - 1 <= wave_min_lim;  // uniform: no key past any row's limit
+    if (key_base + kPfKeys > kend) {  // V rows at or past kend (poison, or block 0) must not reach O
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        uint32_t mlo = 0u, mhi = 0u;
+        const int k0 = key_base + 16 * kh + 4 * jq;
+        mlo |= (k0 + 0 < kend) ? 0x0000FFFFu : 0u;
+        mlo |= (k0 + 1 < kend) ? 0xFFFF0000u : 0u;
+        mhi |= (k0 + 2 < kend) ? 0x0000FFFFu : 0u;
+        mhi |= (k0 + 3 < kend) ? 0xFFFF0000u : 0u;
+        const uint64_t msk = (static_cast<uint64_t>(mhi) << 32) | mlo;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          vop[kh][nb] = __builtin_bit_cast(f16x4, __builtin_bit_cast(uint64_t, vop[kh][nb]) & msk);
+      }
+    }
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+      f32x4 sc[2];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kh][kb], qop[nr][kb], acc, 0, 0, 0);
+        sc[kh] = acc;
+      }
+      bool ok[2][4];
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ok[kh][i] = causal_free || (key_base + 16 * kh + 4 * jq + i <= lim[nr]);
+          mt = fmaxf(mt, ok[kh][i] ? sc[kh][i] : -INFINITY);
+        }
+      {
+        const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
+        mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
+        const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
+        mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
+      }
+      mt *= a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m[nr] + kRebase) != 0) {
+        const float m_new = fmaxf(m[nr], mt);
+        const float corr = rescale(m[nr], m_new);
+        l[nr] *= corr;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nr][nb] *= corr;
+        m[nr] = m_new;
+      }
+      float p[2][4];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[kh][i] = ok[kh][i] ? __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr])) : 0.0f;
+          l[nr] += p[kh][i];
+        }
+      const f16x8 pb = {static_cast<f16>(p[0][0]), static_cast<f16>(p[0][1]), static_cast<f16>(p[0][2]),
+                        static_cast<f16>(p[0][3]), static_cast<f16>(p[1][0]), static_cast<f16>(p[1][1]),
+                        static_cast<f16>(p[1][2]), static_cast<f16>(p[1][3])};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const f16x8 vt = {vop[0][nb][0], vop[0][nb][1], vop[0][nb][2], vop[0][nb][3],
+                          vop[1][nb][0], vop[1][nb][1], vop[1][nb][2], vop[1][nb][3]};
+        o[nr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vt, pb, o[nr][nb], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- prologue: the flag, then the first NST - 1 tiles
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  {
+    int32_t pe[2];
+    load_entries2(entry_ptr(0), entry_ptr(1), pe);
+    fetch(0, 0, pe[0]);
+    fetch(1, 1, pe[1]);
+  }
+  static_assert(NST == 3, "the prologue fills two stages");
+  f16x8 kop[2][KB];
+  f16x4 vop[2][NB];
+  for (int i0 = 0; i0 < T; i0 += NST) {
+    unroll<NST>([&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int nxt = (st + NST - 1) % NST;
+      const int i = i0 + st;
+      if (i >= T) return;
+      int32_t pn;
+      if constexpr (D == 128) pf_read_d128<VM, st * STAGE, ROW>(ka, va, kop, vop, entry_ptr(i + NST - 1), pn);
+      else pf_read_d64<VM, st * STAGE, ROW>(ka, va, kop, vop, entry_ptr(i + NST - 1), pn);
+      fetch(i + NST - 1, nxt, pn);
+      consume(i, kop, vop);
+    });
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS
+  if (bad) s_bad = 1;
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
+
+  // ---- rows: o / l, or NaN when a table entry was outside the pool
+#pragma unroll
+  for (int nr = 0; nr < NR; ++nr) {
+    float lt = l[nr];
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(lt), as_u(lt), false, false);
+      lt = as_f(x32[0]) + as_f(x32[1]);
+      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(lt), as_u(lt), false, false);
+      lt = as_f(x16[0]) + as_f(x16[1]);
+    }
+    if (!rvalid[nr]) continue;
+    const int r = row_lo + 64 * w + 16 * nr + g;
+    const float inv = any_bad ? __builtin_nanf("") : 1.0f / lt;
+    f16* dst = out_row(r / G, r % G);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const f32x4 y = o[nr][nb] * inv;
+      *reinterpret_cast<f16x4*>(dst + 16 * nb + 4 * jq) =
+          f16x4{static_cast<f16>(y[0]), static_cast<f16>(y[1]), static_cast<f16>(y[2]), static_cast<f16>(y[3])};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // decode, second launch (pa_decode_reduce only; pa_decode merges in its one launch): one
 // wave per (sequence, query head).  Empty or invalid contexts get their zero or NaN row
 // here; a segment held whole by one wave was written by it; a segment split over waves
@@ -1904,6 +2315,13 @@ int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, v
 
 bool valid_scale(float x) { return x > 0.0f && std::isfinite(x); }
 
+template <int D>
+int launch_prefill(const PrefillArgs& a, int num_seqs, hipStream_t stream) {
+  hipLaunchKernelGGL((pa_prefill_kernel<D>), dim3(a.n_row_blocks, a.num_kv_heads, num_seqs),
+                     dim3(kPfWaves * kWave), 0, stream, a);
+  return check_hip("pa_prefill_kernel launch");
+}
+
 DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, float scale,
                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
@@ -2129,6 +2547,65 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
   return decode_fp8(1, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
                     block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                     max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+               const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+               float scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+               int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+               int32_t max_query_len, int32_t max_context_len, int64_t num_blocks, int32_t dtype,
+               void* stream) {
+  g_error.clear();
+  int rc = check_common(dtype, head_dim, block_size);
+  if (rc != PA_OK) return rc;
+  if (dtype != PA_F16) return fail(PA_ERR_UNSUPPORTED, "pa_prefill is built for PA_F16 only");
+  if (!valid_scale(scale))
+    return fail(PA_ERR_INVALID_ARG, "scale %g must be positive and finite", static_cast<double>(scale));
+  if (num_seqs < 0 || max_query_len < 0 || max_context_len < 0)
+    return fail(PA_ERR_INVALID_ARG, "num_seqs, max_query_len and max_context_len must be >= 0");
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if (max_blocks_per_seq <= 0) return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d must be > 0", max_blocks_per_seq);
+  if (num_blocks <= 0 || num_blocks > (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "num_blocks %lld outside [1, 2^31 - 1]", (long long)num_blocks);
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks_per_seq * block_size", max_context_len);
+  if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
+  if (static_cast<int64_t>(num_kv_heads) * block_size * head_dim * 2 > (static_cast<int64_t>(1) << 32) - 1)
+    return fail(PA_ERR_INVALID_ARG, "one block of one layer exceeds 4 GiB");
+  const int group = num_q_heads / num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(max_query_len) * group;
+  if (rows > (static_cast<int64_t>(1) << 30))
+    return fail(PA_ERR_INVALID_ARG, "max_query_len * group above 2^30 rows per sequence");
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start)
+    return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4))
+    return fail(PA_ERR_INVALID_ARG, "block_tables, context_lens and query_start must be 4-byte aligned");
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.block_size = block_size;
+  a.log2_block = log2_of(block_size);
+  a.num_kv_heads = num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.group = group;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_query_len = max_query_len;
+  a.max_context_len = max_context_len;
+  a.num_blocks = num_blocks;
+  a.n_row_blocks = static_cast<int>((rows + kPfRows - 1) / kPfRows);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  return head_dim == 64 ? launch_prefill<64>(a, num_seqs, st) : launch_prefill<128>(a, num_seqs, st);
 }
 
 }  // extern "C"

@@ -26,7 +26,8 @@ def test_header_declares_the_calls():
     names = _declared_functions()
     for want in ("pa_cache_write", "pa_decode", "pa_decode_workspace_bytes",
                  "pa_decode_partitions", "pa_decode_reduce", "pa_last_error", "pa_abi_version",
-                 "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_fp8_partitions"):
+                 "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_fp8_partitions",
+                 "pa_prefill"):
         assert want in names
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 1
+    assert P.lib().pa_abi_version() == (2 << 16) | 2
 
 
 def test_workspace_size_query():
@@ -216,6 +217,40 @@ def test_fp8_binding_checks_element_types():
         P.pa_decode_fp8(h, h, h, h, None, None, 0.1, 1.0, 1.0, 16, 8)
     with pytest.raises(P.PaError, match="uint8"):
         P.pa_cache_write_fp8(h, h, None, h, h, 1.0, 1.0)
+
+
+def _prefill(**over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, qs=FAKE, scale=0.1, B=16,
+             hkv=8, S=4, hq=32, D=128, mb=16, mql=64, mcl=256, N=100, dt=_lib.PA_F16, stream=None)
+    a.update(over)
+    return P.lib().pa_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["qs"],
+                              a["scale"], a["B"], a["hkv"], a["S"], a["hq"], a["D"], a["mb"],
+                              a["mql"], a["mcl"], a["N"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dt=_lib.PA_F32), _lib.PA_ERR_UNSUPPORTED),
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(B=4), _lib.PA_ERR_UNSUPPORTED),
+    (dict(scale=0.0), _lib.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(hq=30), _lib.PA_ERR_INVALID_ARG),
+    (dict(mql=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(mcl=257), _lib.PA_ERR_INVALID_ARG),
+    (dict(N=0), _lib.PA_ERR_INVALID_ARG),
+    (dict(S=70000), _lib.PA_ERR_INVALID_ARG),
+    (dict(qs=None), _lib.PA_ERR_INVALID_ARG),
+    (dict(qs=FAKE + 2), _lib.PA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), _lib.PA_ERR_INVALID_ARG),
+])
+def test_prefill_rejects_bad_arguments(over, code):
+    assert _prefill(**over) == code
+    assert P.last_error() != ""
+
+
+def test_prefill_with_nothing_to_do_is_a_no_op():
+    assert _prefill(S=0, out=None, q=None) == _lib.PA_OK
+    assert _prefill(mql=0, out=None, q=None) == _lib.PA_OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
