@@ -1557,8 +1557,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 // ---------------------------------------------------------------------------
 
 constexpr int kPfWaves = 4;                            // waves per work-group
-constexpr int kPfBlocks = 4;                           // 16-row product blocks per wave
-constexpr int kPfRows = kPfWaves * kPfBlocks * 16;     // query rows per work-group
+constexpr int kPfInterleave = 2;                       // blocks whose score products interleave
 constexpr int kPfKeys = 32;                            // keys per tile
 constexpr int kPfStages = 3;
 
@@ -1680,12 +1679,15 @@ __device__ __forceinline__ void pf_read_d64(const uint32_t (&ka)[2], const uint3
       : "memory");
 }
 
-template <int D>
+// NR 16-row product blocks per wave, an NST-stage ring
+template <int D, int NR, int NST>
 __global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const PrefillArgs a) {
   using C = PCfg<D>;
   constexpr int ROW = C::kRow, NC = C::kNC, TILE = C::kTile, STAGE = C::kStage;
-  constexpr int LOADS = C::kLoads, KB = C::kKB, NB = C::kNB, NR = kPfBlocks, NST = kPfStages;
-  constexpr int VM = (NST - 2) * 2 * LOADS;  // loads younger than the stage being read
+  constexpr int LOADS = C::kLoads, KB = C::kKB, NB = C::kNB;
+  constexpr int kPfRows = kPfWaves * NR * 16;  // query rows per work-group
+  constexpr int VM = (NST - 2) * 2 * LOADS;    // loads younger than the stage being read
+  static_assert(NST >= 2 && NST <= 4, "ring depth");
   static_assert(NST * STAGE + 16 * ROW <= 65536, "LDS offsets are 16-bit immediates");
   __shared__ __align__(1024) char s_ring[NST * STAGE];
   __shared__ int s_bad;
@@ -1719,14 +1721,14 @@ __global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const Pref
   const int kend = ctx - n + t_last + 1;  // keys the work-group needs: 0 .. kend - 1 (<= ctx)
   const int T = (kend + kPfKeys - 1) / kPfKeys;
 
-  // ---- query rows of this lane: row 64 w + 16 nr + g of the block; its position limit
+  // ---- query rows of this lane: row 16 NR w + 16 nr + g of the block; its position limit
   int lim[NR];
   bool rvalid[NR];
   f16x8 qop[NR][KB];
   int wave_min_lim = 0x7FFFFFFF;
 #pragma unroll
   for (int nr = 0; nr < NR; ++nr) {
-    const int r = row_lo + 64 * w + 16 * nr + g;
+    const int r = row_lo + 16 * NR * w + 16 * nr + g;
     rvalid[nr] = r < row_hi;
     const int t = r / G;
     lim[nr] = rvalid[nr] ? ctx - n + t : kend - 1;  // last key the row sees
@@ -1806,10 +1808,58 @@ __global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const Pref
     for (int nb = 0; nb < NB; ++nb) o[nr][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  auto consume = [&](int f, const f16x8 (&kop)[2][KB], f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
+  // Softmax of block nr over the tile, then its P.V products; unmasked: no key of the tile
+  // lies past any row's limit.  (Separate code for unmasked tiles was measured slower: it
+  // raises register pressure more than it saves.)
+  auto block_pv = [&](auto nrc, int key_base, bool unmasked, const f32x4 (&sc)[2],
+                      const f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
+    constexpr int nr = decltype(nrc)::value;
     constexpr float kRebase = 8.0f;
+    bool ok[2][4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ok[kh][i] = unmasked || (key_base + 16 * kh + 4 * jq + i <= lim[nr]);
+        mt = fmaxf(mt, ok[kh][i] ? sc[kh][i] : -INFINITY);
+      }
+    {
+      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
+      mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
+      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
+      mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
+    }
+    mt *= a.scale_log2;
+    if (__builtin_amdgcn_ballot_w64(mt > m[nr] + kRebase) != 0) {
+      const float m_new = fmaxf(m[nr], mt);
+      const float corr = rescale(m[nr], m_new);
+      l[nr] *= corr;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nr][nb] *= corr;
+      m[nr] = m_new;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kh][i] = ok[kh][i] ? __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr])) : 0.0f;
+        l[nr] += p[kh][i];
+      }
+    const f16x8 pb = {static_cast<f16>(p[0][0]), static_cast<f16>(p[0][1]), static_cast<f16>(p[0][2]),
+                      static_cast<f16>(p[0][3]), static_cast<f16>(p[1][0]), static_cast<f16>(p[1][1]),
+                      static_cast<f16>(p[1][2]), static_cast<f16>(p[1][3])};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const f16x8 vt = {vop[0][nb][0], vop[0][nb][1], vop[0][nb][2], vop[0][nb][3],
+                        vop[1][nb][0], vop[1][nb][1], vop[1][nb][2], vop[1][nb][3]};
+      o[nr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vt, pb, o[nr][nb], 0, 0, 0);
+    }
+  };
+
+  auto consume = [&](int f, const f16x8 (&kop)[2][KB], f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
     const int key_base = f * kPfKeys;
-    const bool causal_free = key_base + kPfKeys - 1 <= wave_min_lim;  // uniform: no key past any row's limit
     if (key_base + kPfKeys > kend) {  // V rows at or past kend (poison, or block 0) must not reach O
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
@@ -1825,70 +1875,45 @@ __global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const Pref
           vop[kh][nb] = __builtin_bit_cast(f16x4, __builtin_bit_cast(uint64_t, vop[kh][nb]) & msk);
       }
     }
+    // uniform: no key of the tile lies past any row's limit
+    const bool unmasked = key_base + kPfKeys - 1 <= wave_min_lim;
+    // blocks in groups of NI: the scores of a group with the dim chunk outermost, so its
+    // 2 NI accumulation chains interleave, then each block's softmax and P.V
+    constexpr int NI = kPfInterleave < NR ? kPfInterleave : NR;
+    static_assert(NR % NI == 0, "whole groups");
+    unroll<NR / NI>([&](auto gc) __attribute__((always_inline)) {
+      constexpr int g0 = decltype(gc)::value * NI;
+      f32x4 sc[NI][2];
 #pragma unroll
-    for (int nr = 0; nr < NR; ++nr) {
-      f32x4 sc[2];
+      for (int b = 0; b < NI; ++b) sc[b][0] = sc[b][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kh][kb], qop[nr][kb], acc, 0, 0, 0);
-        sc[kh] = acc;
-      }
-      bool ok[2][4];
-      float mt = -INFINITY;
+        for (int b = 0; b < NI; ++b)
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[kh][i] = causal_free || (key_base + 16 * kh + 4 * jq + i <= lim[nr]);
-          mt = fmaxf(mt, ok[kh][i] ? sc[kh][i] : -INFINITY);
-        }
-      {
-        const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
-        mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
-        const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
-        mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
-      }
-      mt *= a.scale_log2;
-      if (__builtin_amdgcn_ballot_w64(mt > m[nr] + kRebase) != 0) {
-        const float m_new = fmaxf(m[nr], mt);
-        const float corr = rescale(m[nr], m_new);
-        l[nr] *= corr;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nr][nb] *= corr;
-        m[nr] = m_new;
-      }
-      float p[2][4];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kh][i] = ok[kh][i] ? __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr])) : 0.0f;
-          l[nr] += p[kh][i];
-        }
-      const f16x8 pb = {static_cast<f16>(p[0][0]), static_cast<f16>(p[0][1]), static_cast<f16>(p[0][2]),
-                        static_cast<f16>(p[0][3]), static_cast<f16>(p[1][0]), static_cast<f16>(p[1][1]),
-                        static_cast<f16>(p[1][2]), static_cast<f16>(p[1][3])};
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const f16x8 vt = {vop[0][nb][0], vop[0][nb][1], vop[0][nb][2], vop[0][nb][3],
-                          vop[1][nb][0], vop[1][nb][1], vop[1][nb][2], vop[1][nb][3]};
-        o[nr][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vt, pb, o[nr][nb], 0, 0, 0);
-      }
-    }
+          for (int kh = 0; kh < 2; ++kh)
+            sc[b][kh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kh][kb], qop[g0 + b][kb], sc[b][kh], 0, 0, 0);
+      unroll<NI>([&](auto bc) __attribute__((always_inline)) {
+        constexpr int b = decltype(bc)::value;
+        block_pv(std::integral_constant<int, g0 + b>{}, key_base, unmasked, sc[b], vop);
+      });
+    });
   };
 
   // ---- prologue: the flag, then the first NST - 1 tiles
   if (threadIdx.x == 0) s_bad = 0;
   __syncthreads();
-  {
+  if constexpr (NST == 3) {
     int32_t pe[2];
     load_entries2(entry_ptr(0), entry_ptr(1), pe);
     fetch(0, 0, pe[0]);
     fetch(1, 1, pe[1]);
+  } else {
+    unroll<NST - 1>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      fetch(j, j, scalar_load(entry_ptr(j)));
+    });
   }
-  static_assert(NST == 3, "the prologue fills two stages");
   f16x8 kop[2][KB];
   f16x4 vop[2][NB];
   for (int i0 = 0; i0 < T; i0 += NST) {
@@ -1920,7 +1945,7 @@ __global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const Pref
       lt = as_f(x16[0]) + as_f(x16[1]);
     }
     if (!rvalid[nr]) continue;
-    const int r = row_lo + 64 * w + 16 * nr + g;
+    const int r = row_lo + 16 * NR * w + 16 * nr + g;
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / lt;
     f16* dst = out_row(r / G, r % G);
 #pragma unroll
@@ -2315,11 +2340,24 @@ int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, v
 
 bool valid_scale(float x) { return x > 0.0f && std::isfinite(x); }
 
-template <int D>
-int launch_prefill(const PrefillArgs& a, int num_seqs, hipStream_t stream) {
-  hipLaunchKernelGGL((pa_prefill_kernel<D>), dim3(a.n_row_blocks, a.num_kv_heads, num_seqs),
+template <int D, int NR>
+int launch_prefill_rows(PrefillArgs a, int64_t rows, int num_seqs, hipStream_t stream) {
+  constexpr int kRows = kPfWaves * NR * 16;
+  a.n_row_blocks = static_cast<int>((rows + kRows - 1) / kRows);
+  hipLaunchKernelGGL((pa_prefill_kernel<D, NR, kPfStages>), dim3(a.n_row_blocks, a.num_kv_heads, num_seqs),
                      dim3(kPfWaves * kWave), 0, stream, a);
   return check_hip("pa_prefill_kernel launch");
+}
+
+// Rows per wave: 64 (four 16-row blocks, one wave per SIMD) serve each K/V tile to the most
+// rows and were fastest for chunks after a long cached prefix; 16 (two waves per SIMD, more
+// and shorter work-groups) were fastest where the chunks make up most of the context, the
+// causal triangle of whole prompts.  Measured on MI355X; chosen from the host bounds.
+template <int D>
+int launch_prefill(const PrefillArgs& a, int64_t rows, int num_seqs, hipStream_t stream) {
+  if (2 * static_cast<int64_t>(a.max_query_len) >= a.max_context_len)
+    return launch_prefill_rows<D, 1>(a, rows, num_seqs, stream);
+  return launch_prefill_rows<D, 4>(a, rows, num_seqs, stream);
 }
 
 DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -2603,9 +2641,9 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.max_query_len = max_query_len;
   a.max_context_len = max_context_len;
   a.num_blocks = num_blocks;
-  a.n_row_blocks = static_cast<int>((rows + kPfRows - 1) / kPfRows);
+  a.n_row_blocks = 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  return head_dim == 64 ? launch_prefill<64>(a, num_seqs, st) : launch_prefill<128>(a, num_seqs, st);
+  return head_dim == 64 ? launch_prefill<64>(a, rows, num_seqs, st) : launch_prefill<128>(a, rows, num_seqs, st);
 }
 
 }  // extern "C"

@@ -93,6 +93,10 @@ SMALL = [
     (64, 8, 16, 1, [130, 40], [66, 40]),
     (128, 16, 16, 1, [300, 33], [31, 33]),
     (64, 32, 6, 2, [1024], [300]),
+    # chunks that are most of their context (whole prompts): the 16-rows-per-wave variant
+    (128, 16, 8, 2, [300, 64, 1, 130], [300, 64, 1, 100]),
+    (64, 8, 28, 4, [200, 17], [150, 17]),
+    (128, 32, 16, 2, [257], [257]),
 ]
 
 
@@ -157,8 +161,15 @@ def _mid(B=16, D=128):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-def test_block_size_invariance_bit_identical(D):
-    outs = [_run(c, _to_device(c)) for c in (_mid(8, D), _mid(16, D), _mid(32, D))]
+@pytest.mark.parametrize("whole", [False, True])
+def test_block_size_invariance_bit_identical(D, whole):
+    def mk(B):
+        if not whole:
+            return _mid(B, D)
+        return W.make_prefill_case(seed=33, logical_seed=34, dtype=np.float16, context_lens=[700, 45],
+                                   query_lens=[700, 45], num_q_heads=16, num_kv_heads=4, head_dim=D,
+                                   block_size=B, sigma=0.5)
+    outs = [_run(c, _to_device(c)) for c in (mk(8), mk(16), mk(32))]
     assert outs[0].tobytes() == outs[1].tobytes() == outs[2].tobytes()
 
 
