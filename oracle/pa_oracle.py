@@ -42,6 +42,9 @@ K/V, permutation / block-size / sharing invariants, closed forms); the FP8 part
 ([CON] section 6) by ``tests/test_oracle_fp8.py`` (code values fixed by the E4M3
 definition, torch's float8_e4m3fn table and rounding, brute-force nearest code,
 ties, saturation, and lossless round trips that reduce FP8 decode to the fp64 one);
+``copy_blocks`` and ``BlockManager`` by ``tests/test_oracle_blocks.py`` (every sequence
+reads back its own token history through random forks, appends, frees and swaps; reference
+counts equal table references; planted copy-on-write mistakes are caught);
 ``prefill`` by ``tests/test_oracle_prefill.py`` (torch SDPA with a causal or bottom-right
 mask in float64, pure-Python loops, reduction to ``decode`` at one token per sequence,
 chunk-split invariance).
@@ -259,6 +262,104 @@ def decode_one_partitioned(q, k_cache, v_cache, block_tables, context_lens, scal
         num += w * o_p
         den += w
     return num / den
+
+
+# ---------------------------------------------------------------------------
+# Block copies and the block manager  ([SRC] section 3.2: the free pool, allocate,
+# append a token; [SRC] section 3.3: swap a preempted sequence's blocks out to CPU
+# memory; [DRV] section 4 and [SOSP] section 2.4: several tables point at one block,
+# reference counts and copy-on-write protect writes; [CON] section 4.3).
+# Readings where the pages are silent: the free list is a stack (a released block is
+# the next one handed out) over an initial order; a copy-on-write happens when a token
+# is appended into a partly filled block that another table also points at; a swap
+# moves every distinct block of a group of tables once, keeping their sharing.
+# ---------------------------------------------------------------------------
+
+def copy_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Copies of the destination pools with dst[d] = src[s] for every (s, d) pair, in
+    order; a pair naming a block outside its pool is skipped.  All kv heads, slots and
+    dims of a block move together: a block is the unit of sharing and of swapping."""
+    dk, dv = np.array(dst_k, copy=True), np.array(dst_v, copy=True)
+    for s_blk, d_blk in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        if not (0 <= s_blk < len(src_k) and 0 <= d_blk < len(dk)):
+            continue
+        dk[d_blk] = src_k[s_blk]
+        dv[d_blk] = src_v[s_blk]
+    return dk, dv
+
+
+class BlockManager:
+    """Reference counts over a pool of num_blocks physical blocks of block_size slots."""
+
+    def __init__(self, num_blocks: int, block_size: int, order=None):
+        self.block_size = int(block_size)
+        order = list(range(num_blocks)) if order is None else [int(b) for b in order]
+        assert sorted(order) == list(range(num_blocks)), "order must be a permutation"
+        self.free = order[::-1]  # a stack: the first block of order is handed out first
+        self.refcount = [0] * num_blocks
+
+    def allocate(self) -> int:
+        if not self.free:
+            raise MemoryError("no free block")
+        b = self.free.pop()
+        self.refcount[b] = 1
+        return b
+
+    def share(self, b: int) -> None:
+        assert self.refcount[b] > 0
+        self.refcount[b] += 1
+
+    def release(self, b: int) -> None:
+        assert self.refcount[b] > 0
+        self.refcount[b] -= 1
+        if self.refcount[b] == 0:
+            self.free.append(b)
+
+    def append_slot(self, table: list, ctx: int):
+        """Slot of the token at position ctx of a sequence whose table is `table` (list of
+        block ids, updated in place), and the (source, destination) copy it needs or None.
+        A new block is taken when the position starts one; a shared last block is first
+        copied into a block of its own."""
+        idx, off = divmod(int(ctx), self.block_size)
+        cow = None
+        if off == 0:
+            assert idx == len(table)
+            table.append(self.allocate())
+        else:
+            last = table[idx]
+            if self.refcount[last] > 1:
+                new = self.allocate()
+                self.release(last)
+                table[idx] = new
+                cow = (last, new)
+        return table[idx] * self.block_size + off, cow
+
+    def fork(self, table: list) -> list:
+        """A second table over the same blocks (parallel sampling of one prompt)."""
+        for b in table:
+            self.share(b)
+        return list(table)
+
+    def free_table(self, table: list) -> None:
+        for b in table:
+            self.release(b)
+        table.clear()
+
+    def move(self, tables: list, dst: "BlockManager") -> list:
+        """Move every block of the given tables to the pool dst manages: each distinct block
+        once, the tables rewritten in place, sharing among them kept.  Returns the
+        (source, destination) copies, in the order the blocks are first met."""
+        mapping, pairs = {}, []
+        for table in tables:
+            for j, b in enumerate(table):
+                if b not in mapping:
+                    mapping[b] = dst.allocate()
+                    pairs.append((b, mapping[b]))
+                else:
+                    dst.share(mapping[b])
+                self.release(b)
+                table[j] = mapping[b]
+        return pairs
 
 
 # ---------------------------------------------------------------------------
