@@ -56,6 +56,7 @@ extern "C" {
 #define PA_ERR_UNSUPPORTED (-2) /* valid but not built: dtype, head_dim or block_size     */
 #define PA_ERR_WORKSPACE (-3)   /* workspace missing or smaller than the size query says */
 #define PA_ERR_HIP (-4)         /* a HIP launch failed                                   */
+#define PA_ERR_EXHAUSTED (-5)   /* the block allocator has no free block left             */
 
 /*
  * pa_cache_write -- store each new token's K and V into its slot of the pools.
@@ -246,12 +247,73 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
                int32_t max_query_len, int32_t max_context_len, int64_t num_blocks, int32_t dtype,
                void* stream);
 
+/*
+ * Block copies and the block allocator: sharing, copy-on-write and swap.
+ * [SRC] section 3.2 (a free pool of blocks, allocate on demand, append a token into the
+ * last block or a new one), section 3.3 (preempt by swapping a sequence's blocks out to
+ * CPU memory); [DRV] section 4 and [SOSP] section 2.4 (several tables point at one block;
+ * reference counts and copy-on-write protect writes); [CON] section 4.3.
+ *
+ * pa_copy_blocks -- for every pair i: dst_k[pairs[2i+1]] = src_k[pairs[2i]] and the same for
+ * V, a block being block_bytes bytes (num_kv_heads * block_size * head_dim * element size
+ * for the pools of this library).  Each of the four pools may be device memory of the
+ * current device or pinned host memory (hipHostMalloc, torch pin_memory): the same call
+ * copies within a pool (copy-on-write), between device pools, and to and from host pools
+ * (swap).  The pools are resolved with hipPointerGetAttributes before anything is launched;
+ * memory of another kind is refused.  A pair naming a block outside its pool is skipped.
+ * No destination may also be the source of another pair of the same call, and the source
+ * and destination ranges of one pair must not overlap.
+ *
+ * pairs          [num_pairs, 2] int32 (source, destination), device or pinned host memory
+ * src_num_blocks, dst_num_blocks: blocks in the source and destination pools
+ * returns PA_OK, or a negative code with nothing launched.
+ */
+int pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                   const int32_t* pairs, int32_t num_pairs, int64_t src_num_blocks,
+                   int64_t dst_num_blocks, int64_t block_bytes, void* stream);
+
+/*
+ * pa_allocator -- host-side reference-counted allocator of one pool's blocks.
+ * Free blocks form a stack over an initial order (order[0] is handed out first; NULL means
+ * 0, 1, 2, ...); a released block is the next one handed out.  Each call either completes
+ * or changes nothing (a refused call returns an error code and pa_last_error says why).
+ * Not thread-safe: one allocator, one thread at a time.  Tables are host int32 arrays.
+ *
+ * pa_allocator_append_slot -- the slot of the token at position ctx of a sequence whose
+ *   table holds *num_table_blocks entries (capacity at most): a position that starts a
+ *   block takes a new block (appended to the table); a position inside a last block that
+ *   other tables share first moves the table onto a fresh block, returned as the copy
+ *   (*cow_src, *cow_dst) the caller must make with pa_copy_blocks before writing (both -1
+ *   when none is needed).  Returns PA_ERR_EXHAUSTED with nothing changed when no block is free.
+ * pa_allocator_fork -- child = table, every block shared once more (parallel sampling).
+ * pa_allocator_free_table -- release every entry of a table.
+ * pa_allocator_move -- rewrite num_tables tables (row t: lens[t] entries at tables + t * stride)
+ *   onto the pool of dst: each distinct block once (shared blocks stay shared), writing the
+ *   (source, destination) copies to pairs and their count to *num_pairs; the blocks are
+ *   released in src.  For swap out (device allocator to host allocator) and back.
+ */
+typedef struct pa_allocator pa_allocator;
+pa_allocator* pa_allocator_create(int32_t num_blocks, int32_t block_size, const int32_t* order);
+void pa_allocator_destroy(pa_allocator* a);
+int32_t pa_allocator_num_free(const pa_allocator* a);
+int32_t pa_allocator_refcount(const pa_allocator* a, int32_t block);
+int pa_allocator_allocate(pa_allocator* a, int32_t* block);
+int pa_allocator_share(pa_allocator* a, int32_t block);
+int pa_allocator_release(pa_allocator* a, int32_t block);
+int pa_allocator_append_slot(pa_allocator* a, int32_t* table, int32_t capacity, int32_t* num_table_blocks,
+                             int32_t ctx, int64_t* slot, int32_t* cow_src, int32_t* cow_dst);
+int pa_allocator_fork(pa_allocator* a, const int32_t* table, int32_t n, int32_t* child);
+int pa_allocator_free_table(pa_allocator* a, const int32_t* table, int32_t n);
+int pa_allocator_move(pa_allocator* src, pa_allocator* dst, int32_t* tables, const int32_t* lens,
+                      int32_t num_tables, int32_t stride, int32_t* pairs, int32_t pairs_capacity,
+                      int32_t* num_pairs);
+
 /* Description of the last error on the calling thread ("" if none); valid until the next call. */
 const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 2)
+#define PA_ABI_VERSION ((2 << 16) | 3)
 
 #ifdef __cplusplus
 }

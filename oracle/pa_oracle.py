@@ -349,6 +349,8 @@ class BlockManager:
         """Move every block of the given tables to the pool dst manages: each distinct block
         once, the tables rewritten in place, sharing among them kept.  Returns the
         (source, destination) copies, in the order the blocks are first met."""
+        if len({b for table in tables for b in table}) > len(dst.free):
+            raise MemoryError("not enough free blocks in the destination pool")  # nothing moved
         mapping, pairs = {}, []
         for table in tables:
             for j, b in enumerate(table):

@@ -5,12 +5,14 @@ include/pa.h); this package is its Python binding.
 """
 from ._lib import (  # noqa: F401
     DEFAULT_PARTITION,
+    BlockAllocator,
     PA_F16,
     PA_F32,
     PaError,
     last_error,
     lib,
     pa_cache_write,
+    pa_copy_blocks,
     pa_cache_write_fp8,
     pa_decode,
     pa_decode_fp8,

@@ -22,6 +22,7 @@ PA_ERR_INVALID_ARG = -1
 PA_ERR_UNSUPPORTED = -2
 PA_ERR_WORKSPACE = -3
 PA_ERR_HIP = -4
+PA_ERR_EXHAUSTED = -5
 
 DEFAULT_PARTITION = 0  # 0: as many persistent waves as the GPU holds
 
@@ -55,6 +56,19 @@ SIGNATURES = {
     "pa_prefill": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
                               _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64,
                               _c_int32, _vp]),
+    "pa_copy_blocks": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _c_int32, _c_int64, _c_int64, _c_int64,
+                                  _vp]),
+    "pa_allocator_create": (_vp, [_c_int32, _c_int32, _vp]),
+    "pa_allocator_destroy": (None, [_vp]),
+    "pa_allocator_num_free": (_c_int32, [_vp]),
+    "pa_allocator_refcount": (_c_int32, [_vp, _c_int32]),
+    "pa_allocator_allocate": (_c_int32, [_vp, _vp]),
+    "pa_allocator_share": (_c_int32, [_vp, _c_int32]),
+    "pa_allocator_release": (_c_int32, [_vp, _c_int32]),
+    "pa_allocator_append_slot": (_c_int32, [_vp, _vp, _c_int32, _vp, _c_int32, _vp, _vp, _vp]),
+    "pa_allocator_fork": (_c_int32, [_vp, _vp, _c_int32, _vp]),
+    "pa_allocator_free_table": (_c_int32, [_vp, _vp, _c_int32]),
+    "pa_allocator_move": (_c_int32, [_vp, _vp, _vp, _vp, _c_int32, _c_int32, _vp, _c_int32, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_c_int32, []),
 }
@@ -260,3 +274,97 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, context_lens, query_start
         head_dim, max_blocks, int(max_query_len), int(max_context_len), k_cache.shape[0],
         _dtype_code(q), _stream(q, stream))
     _check("pa_prefill", code)
+
+
+def pa_copy_blocks(src_k, src_v, dst_k, dst_v, pairs, stream=None) -> None:
+    """dst[pairs[i, 1]] = src[pairs[i, 0]] for K and V, whole blocks; pools on the device or in
+    pinned host memory; pairs an int32 [n, 2] tensor (device or pinned host)."""
+    import torch
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise PaError("binding", PA_ERR_INVALID_ARG, "pairs must be an int32 [n, 2] tensor")
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise PaError("binding", PA_ERR_INVALID_ARG, "source and destination blocks differ in shape")
+    block_bytes = src_k[0].numel() * src_k.element_size() if src_k.shape[0] else 0
+    dev = dst_k if dst_k.is_cuda else (src_k if src_k.is_cuda else None)
+    st = _stream(dev, stream) if dev is not None else (0 if stream is None else _stream(None, stream))
+    code = lib().pa_copy_blocks(_ptr(src_k), _ptr(src_v), _ptr(dst_k), _ptr(dst_v), _ptr(pairs),
+                                pairs.shape[0], src_k.shape[0], dst_k.shape[0], block_bytes, st)
+    _check("pa_copy_blocks", code)
+
+
+class BlockAllocator:
+    """The library's reference-counted block allocator (host side; see pa.h)."""
+
+    def __init__(self, num_blocks: int, block_size: int, order=None):
+        self.block_size = int(block_size)
+        self._order = None
+        if order is not None:
+            self._order = (ctypes.c_int32 * num_blocks)(*[int(b) for b in order])
+        h = lib().pa_allocator_create(int(num_blocks), self.block_size, self._order)
+        if not h:
+            raise PaError("pa_allocator_create", PA_ERR_INVALID_ARG, last_error())
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_allocator_destroy(h)
+            self._h = None
+
+    @property
+    def num_free(self) -> int:
+        return int(lib().pa_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib().pa_allocator_refcount(self._h, int(block)))
+
+    def allocate(self) -> int:
+        b = ctypes.c_int32()
+        _check("pa_allocator_allocate", lib().pa_allocator_allocate(self._h, ctypes.byref(b)))
+        return b.value
+
+    def share(self, block: int) -> None:
+        _check("pa_allocator_share", lib().pa_allocator_share(self._h, int(block)))
+
+    def release(self, block: int) -> None:
+        _check("pa_allocator_release", lib().pa_allocator_release(self._h, int(block)))
+
+    def append_slot(self, table: list, ctx: int, capacity: int = 1 << 16):
+        """Slot of position ctx of the sequence whose table (a list, updated in place) is given,
+        and the (source, destination) copy to make first, or None."""
+        buf = (ctypes.c_int32 * max(capacity, len(table) + 1))(*table)
+        n = ctypes.c_int32(len(table))
+        slot, cs, cd = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check("pa_allocator_append_slot", lib().pa_allocator_append_slot(
+            self._h, buf, len(buf), ctypes.byref(n), int(ctx), ctypes.byref(slot), ctypes.byref(cs),
+            ctypes.byref(cd)))
+        table[:] = list(buf[:n.value])
+        return slot.value, (None if cs.value < 0 else (cs.value, cd.value))
+
+    def fork(self, table: list) -> list:
+        src = (ctypes.c_int32 * max(len(table), 1))(*table)
+        child = (ctypes.c_int32 * max(len(table), 1))()
+        _check("pa_allocator_fork", lib().pa_allocator_fork(self._h, src, len(table), child))
+        return list(child[:len(table)])
+
+    def free_table(self, table: list) -> None:
+        buf = (ctypes.c_int32 * max(len(table), 1))(*table)
+        _check("pa_allocator_free_table", lib().pa_allocator_free_table(self._h, buf, len(table)))
+        table.clear()
+
+    def move(self, tables: list, dst: "BlockAllocator") -> list:
+        """Rewrite the tables (lists, updated in place) onto dst's pool; returns the copies."""
+        stride = max([len(t) for t in tables] + [1])
+        flat = (ctypes.c_int32 * (stride * max(len(tables), 1)))()
+        for i, t in enumerate(tables):
+            for j, b in enumerate(t):
+                flat[i * stride + j] = b
+        lens = (ctypes.c_int32 * max(len(tables), 1))(*[len(t) for t in tables])
+        cap = sum(len(t) for t in tables)
+        pairs = (ctypes.c_int32 * max(2 * cap, 2))()
+        n = ctypes.c_int32()
+        _check("pa_allocator_move", lib().pa_allocator_move(
+            self._h, dst._h, flat, lens, len(tables), stride, pairs, cap, ctypes.byref(n)))
+        for i, t in enumerate(tables):
+            t[:] = list(flat[i * stride:i * stride + len(t)])
+        return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(n.value)]

@@ -53,6 +53,7 @@
 #include <utility>
 
 #include "pa.h"
+#include "pa_internal.h"
 
 namespace {
 
@@ -2000,17 +2001,8 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
 // host side
 // ---------------------------------------------------------------------------
 
-thread_local std::string g_error;
-
-int fail(int code, const char* fmt, ...) {
-  char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
-  va_end(ap);
-  g_error = buf;
-  return code;
-}
+using pa_detail::fail;
+using pa_detail::g_error;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
