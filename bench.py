@@ -61,8 +61,11 @@ def parse():
 
 ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
                "long_context_b16", "long_context_b32", "llama3_8b_fp8", "llama2_70b_fp8",
-               "long_context_b16_fp8", "prefill_llama3_8b", "prefill_llama2_70b"]
+               "long_context_b16_fp8", "prefill_llama3_8b", "prefill_llama2_70b",
+               "copy_blocks_device", "swap_out_host"]
 PREFILL = ("prefill_llama3_8b", "prefill_llama2_70b")
+BLOCK_COPIES = ("copy_blocks_device", "swap_out_host")
+HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, one direction: the host link assumed for swap
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, published
 WORKLOAD_NAMES = {
     "tiny_fp32": "tiny fp32 decode (4 sequences, ctx 1..250)",
@@ -77,6 +80,8 @@ WORKLOAD_NAMES = {
     "long_context_b16_fp8": "32K-128K context decode, block size 16, FP8 E4M3 KV cache",
     "prefill_llama3_8b": "chunked prefill, Llama-3-8B shape: 8 x 512-token chunks after 1K-3.5K cached tokens",
     "prefill_llama2_70b": "whole-prompt prefill, Llama-2-70B shape: 4 prompts of 2048 tokens",
+    "copy_blocks_device": "copy-on-write of 4096 blocks within one device pool (8 kv heads x 16 x 128, fp16)",
+    "swap_out_host": "swap out of 1024 blocks from the device pools to pinned host pools (8 x 16 x 128, fp16)",
 }
 FP8_SUFFIX = "_fp8"
 
@@ -175,7 +180,12 @@ def main():
     import workloads
     workloads.set_progress(log)
     for name in (ALL_CONFIGS if args.config == "all" else [args.config]):
-        result = run_prefill(args, name) if name in PREFILL else run_one(args, name)
+        if name in PREFILL:
+            result = run_prefill(args, name)
+        elif name in BLOCK_COPIES:
+            result = run_block_copies(args, name)
+        else:
+            result = run_one(args, name)
         print(json.dumps(result), flush=True)
         torch.cuda.empty_cache()
 
@@ -491,6 +501,82 @@ def run_prefill(args, config):
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = prefill_cpu_baseline(case)
+    return result
+
+
+def run_block_copies(args, config):
+    """Block copies: copy-on-write within the device pools, or swap out to pinned host pools.
+    One step = one pa_copy_blocks call over all the pairs."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_167_amd as P
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1008)
+    hkv, bsz, d = 8, 16, 128
+    n_pool = 8192
+    device_copy = config == "copy_blocks_device"
+    n_pairs = 4096 if device_copy else 1024
+    k = torch.randn((n_pool, hkv, bsz, d), dtype=torch.float16, device=dev)
+    v = torch.randn_like(k)
+    if device_copy:  # sources in the first half, distinct destinations in the second
+        pairs = np.stack([rng.integers(0, n_pool // 2, n_pairs), n_pool // 2 + rng.permutation(n_pool // 2)[:n_pairs]], 1)
+        dk, dv = k, v
+    else:
+        pairs = np.stack([rng.permutation(n_pool)[:n_pairs], rng.permutation(n_pairs)], 1)
+        dk = torch.empty((n_pairs, hkv, bsz, d), dtype=torch.float16).pin_memory()
+        dv = torch.empty_like(dk).pin_memory()
+    pairs_t = torch.from_numpy(pairs.astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    block_bytes = hkv * bsz * d * 2
+    moved = 2 * n_pairs * block_bytes  # K and V blocks copied
+
+    def step():
+        P.pa_copy_blocks(k, v, dk, dv, pairs_t, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern_ms = e0.elapsed_time(e1) / args.steps
+    # device: every byte read from and written to HBM; host: every byte crosses the host link
+    traffic = 2 * moved if device_copy else moved
+    achieved = traffic / (kern_ms * 1e-3) / 1e9
+    peak = HBM_PEAK_GBS if device_copy else HOST_LINK_GBS
+    result = {
+        "metric": "paged block copy GB/s (copy-on-write / swap)",
+        "value": round(moved / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[config], "name": config, "pairs": n_pairs,
+                   "block_bytes_per_pool": block_bytes, "bytes_copied": moved},
+        "roofline": {"kernel": "pa_copy_blocks_kernel", "bound": "hbm" if device_copy else "host link",
+                     "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "alg_bytes_per_launch": traffic, "avg_launch_us": round(kern_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import pa_oracle as O
+        kc, vc = k[: n_pool // 4].cpu().numpy(), v[: n_pool // 4].cpu().numpy()
+        sub = pairs[(pairs[:, 0] < n_pool // 4)]
+        sub = np.stack([sub[:, 0], np.arange(len(sub)) % (n_pool // 4)], 1)
+        t0 = time.perf_counter()
+        O.copy_blocks(kc, vc, kc, vc, sub)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(2 * len(sub) * block_bytes / dt / 1e9, 3), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{len(sub)} block pairs within a {n_pool // 4}-block host pool"}
     return result
 
 
