@@ -308,12 +308,56 @@ int pa_allocator_move(pa_allocator* src, pa_allocator* dst, int32_t* tables, con
                       int32_t num_tables, int32_t stride, int32_t* pairs, int32_t pairs_capacity,
                       int32_t* num_pairs);
 
+/*
+ * A virtually contiguous K/V cache: the baseline the vAttention page sets against paging
+ * ([VATT] "核心机制" 1-3: reserve virtually contiguous space per request up front, back it
+ * with physical pages only as the KV grows, make sure every active request is backed before
+ * each iteration's kernels; "GPU / 系统数据路径": the kernel addresses the KV as a flat
+ * tensor).  HIP virtual memory (hipMemAddressReserve / hipMemCreate / hipMemMap /
+ * hipMemSetAccess) does the mapping; there are no block tables.  One layer, fp16.
+ *
+ * pa_vkv_create -- reserve K and V address ranges for max_seqs sequences of up to
+ *   max_context_len tokens, laid out [max_seqs][region][num_kv_heads][head_dim] with each
+ *   sequence's region a whole number of pages.  page_bytes 0 picks the smallest page that
+ *   is a multiple of the allocation granularity and of 16 tokens; otherwise it must be such a
+ *   multiple.  Returns NULL on error (see pa_last_error).  Allocates device memory.
+ * pa_vkv_step -- before an iteration: map pages so that tokens [0, context_lens[s]) of every
+ *   sequence s < num_seqs are backed (never unmaps), and record the lengths (host array) for
+ *   pa_decode_dense.  Synchronises the stream.  PA_ERR_EXHAUSTED when memory runs out; the
+ *   call then maps nothing.
+ * pa_vkv_free_seq -- a finished sequence: synchronise the device, unmap its pages.
+ * pa_vkv_write -- store token t's K/V rows at (seq_ids[t], positions[t]) (device int32
+ *   arrays; k, v [num_tokens, num_kv_heads, head_dim] fp16); positions no page backs are
+ *   skipped.
+ * pa_decode_dense -- pa_decode over the cache for the sequences of the last step, with their
+ *   recorded lengths: out, q [num_seqs, num_q_heads, head_dim] fp16; workspace as
+ *   pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+ *   max_context_len, partition_size).  Same kernels, work split and arithmetic as pa_decode
+ *   for fp16, with each tile's address computed instead of looked up.
+ */
+typedef struct pa_vkv pa_vkv;
+pa_vkv* pa_vkv_create(int32_t max_seqs, int32_t max_context_len, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t dtype, int64_t page_bytes);
+void pa_vkv_destroy(pa_vkv* kv);
+int pa_vkv_step(pa_vkv* kv, const int32_t* context_lens, int32_t num_seqs, void* stream);
+int pa_vkv_free_seq(pa_vkv* kv, int32_t seq);
+int pa_vkv_write(pa_vkv* kv, const void* k, const void* v, const int32_t* seq_ids, const int32_t* positions,
+                 int32_t num_tokens, void* stream);
+void* pa_vkv_k(const pa_vkv* kv);
+void* pa_vkv_v(const pa_vkv* kv);
+int64_t pa_vkv_seq_bytes(const pa_vkv* kv);
+int64_t pa_vkv_page_bytes(const pa_vkv* kv);
+int64_t pa_vkv_mapped_bytes(const pa_vkv* kv);
+int32_t pa_vkv_capacity(const pa_vkv* kv, int32_t seq);
+int pa_decode_dense(void* out, const void* q, const pa_vkv* kv, float scale, int32_t num_q_heads,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Description of the last error on the calling thread ("" if none); valid until the next call. */
 const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 3)
+#define PA_ABI_VERSION ((2 << 16) | 4)
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@ include/pa.h); this package is its Python binding.
 from ._lib import (  # noqa: F401
     DEFAULT_PARTITION,
     BlockAllocator,
+    DenseKV,
     PA_F16,
     PA_F32,
     PaError,

@@ -69,6 +69,19 @@ SIGNATURES = {
     "pa_allocator_fork": (_c_int32, [_vp, _vp, _c_int32, _vp]),
     "pa_allocator_free_table": (_c_int32, [_vp, _vp, _c_int32]),
     "pa_allocator_move": (_c_int32, [_vp, _vp, _vp, _vp, _c_int32, _c_int32, _vp, _c_int32, _vp]),
+    "pa_vkv_create": (_vp, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64]),
+    "pa_vkv_destroy": (None, [_vp]),
+    "pa_vkv_step": (_c_int32, [_vp, _vp, _c_int32, _vp]),
+    "pa_vkv_free_seq": (_c_int32, [_vp, _c_int32]),
+    "pa_vkv_write": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _c_int32, _vp]),
+    "pa_vkv_k": (_vp, [_vp]),
+    "pa_vkv_v": (_vp, [_vp]),
+    "pa_vkv_seq_bytes": (_c_int64, [_vp]),
+    "pa_vkv_page_bytes": (_c_int64, [_vp]),
+    "pa_vkv_mapped_bytes": (_c_int64, [_vp]),
+    "pa_vkv_capacity": (_c_int32, [_vp, _c_int32]),
+    "pa_decode_dense": (_c_int32, [_vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32, _vp,
+                                   ctypes.c_size_t, _vp]),
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_c_int32, []),
 }
@@ -368,3 +381,78 @@ class BlockAllocator:
         for i, t in enumerate(tables):
             t[:] = list(flat[i * stride:i * stride + len(t)])
         return [(pairs[2 * i], pairs[2 * i + 1]) for i in range(n.value)]
+
+
+class DenseKV:
+    """The library's virtually contiguous K/V cache (HIP virtual memory, no block tables)."""
+
+    def __init__(self, max_seqs, max_context_len, num_kv_heads, head_dim, page_bytes=0):
+        h = lib().pa_vkv_create(int(max_seqs), int(max_context_len), int(num_kv_heads),
+                                int(head_dim), PA_F16, int(page_bytes))
+        if not h:
+            raise PaError("pa_vkv_create", PA_ERR_INVALID_ARG, last_error())
+        self._h = h
+        self.max_seqs, self.max_context_len = int(max_seqs), int(max_context_len)
+        self.num_kv_heads, self.head_dim = int(num_kv_heads), int(head_dim)
+        self.num_seqs = 0
+
+    def close(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            _lib.pa_vkv_destroy(h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    @property
+    def page_bytes(self) -> int:
+        return int(lib().pa_vkv_page_bytes(self._h))
+
+    @property
+    def seq_bytes(self) -> int:
+        return int(lib().pa_vkv_seq_bytes(self._h))
+
+    @property
+    def mapped_bytes(self) -> int:
+        return int(lib().pa_vkv_mapped_bytes(self._h))
+
+    def capacity(self, seq: int) -> int:
+        return int(lib().pa_vkv_capacity(self._h, int(seq)))
+
+    def step(self, context_lens, stream=None) -> None:
+        """Back tokens [0, context_lens[s]) of every sequence; record the lengths for decode."""
+        n = len(context_lens)
+        arr = (ctypes.c_int32 * max(n, 1))(*[int(c) for c in context_lens])
+        st = 0 if stream is None else (int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream))
+        _check("pa_vkv_step", lib().pa_vkv_step(self._h, arr, n, st))
+        self.num_seqs = n
+
+    def free_seq(self, seq: int) -> None:
+        _check("pa_vkv_free_seq", lib().pa_vkv_free_seq(self._h, int(seq)))
+
+    def write(self, k, v, seq_ids, positions, stream=None) -> None:
+        import torch
+        if k.dtype != torch.float16 or v.dtype != torch.float16:
+            raise PaError("binding", PA_ERR_UNSUPPORTED, "k and v must be float16")
+        if seq_ids.dtype != torch.int32 or positions.dtype != torch.int32:
+            raise PaError("binding", PA_ERR_INVALID_ARG, "seq_ids and positions must be int32")
+        _check("pa_vkv_write", lib().pa_vkv_write(self._h, _ptr(k), _ptr(v), _ptr(seq_ids), _ptr(positions),
+                                                  k.shape[0], _stream(k, stream)))
+
+    def decode(self, out, q, scale, partition_size=DEFAULT_PARTITION, workspace=None, stream=None):
+        """pa_decode over this cache for the sequences and lengths of the last step."""
+        import torch
+        num_seqs, num_q_heads, head_dim = q.shape
+        if num_seqs != self.num_seqs:
+            raise PaError("binding", PA_ERR_INVALID_ARG, f"q has {num_seqs} sequences, the last step {self.num_seqs}")
+        need = pa_decode_workspace_bytes(num_seqs, num_q_heads, self.num_kv_heads, head_dim,
+                                         self.max_context_len, partition_size)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() if workspace is not None else 0
+        _check("pa_decode_dense", lib().pa_decode_dense(
+            _ptr(out), _ptr(q), self._h, float(scale), num_q_heads, int(partition_size), ws_ptr,
+            ws_bytes, _stream(q, stream)))
+        return workspace

@@ -9,7 +9,8 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", "pa_kernels.hip"), os.path.join(HERE, "csrc", "pa_blocks.hip")]
+SOURCES = [os.path.join(HERE, "csrc", "pa_kernels.hip"), os.path.join(HERE, "csrc", "pa_blocks.hip"),
+           os.path.join(HERE, "csrc", "pa_vkv.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"

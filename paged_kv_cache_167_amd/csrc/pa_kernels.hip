@@ -407,6 +407,14 @@ struct StreamArgs {
   int num_waves;
   int rec_rows;     // query rows per piece record
   float out_scale;  // E4M3 pools: the V scale, applied to the normalised output
+  // virtually contiguous cache (no table): sequence s's token p of kv head h is at
+  // dense_k + s * seq_bytes + p * token_bytes + h * row bytes; phantom tiles read guard_k
+  const char* dense_k;
+  const char* dense_v;
+  const char* guard_k;
+  const char* guard_v;
+  int64_t seq_bytes;
+  int64_t token_bytes;
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -952,6 +960,53 @@ __device__ __forceinline__ void read_stage_d64(const uint32_t (&ka)[2], const ui
       : "memory");
 }
 
+// The same reads for the virtually contiguous cache, which has no table entries to load.
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_d128_dense(const uint32_t (&ka)[4], const uint32_t (&va)[8],
+                                                      f16x8 (&k)[4], f16x4 (&v)[8]) {
+  asm volatile(
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b128 %[k1], %[ka1] offset:%[off]\n\t"
+      "ds_read_b128 %[k2], %[ka2] offset:%[off]\n\t"
+      "ds_read_b128 %[k3], %[ka3] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v3], %[va3] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v4], %[va4] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v5], %[va5] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v6], %[va6] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v7], %[va7] offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [k2] "=&v"(k[2]), [k3] "=&v"(k[3]), [v0] "=&v"(v[0]),
+        [v1] "=&v"(v[1]), [v2] "=&v"(v[2]), [v3] "=&v"(v[3]), [v4] "=&v"(v[4]), [v5] "=&v"(v[5]),
+        [v6] "=&v"(v[6]), [v7] "=&v"(v[7])
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [ka2] "v"(ka[2]), [ka3] "v"(ka[3]), [va0] "v"(va[0]),
+        [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]), [va5] "v"(va[5]),
+        [va6] "v"(va[6]), [va7] "v"(va[7]), [vm] "n"(VM), [off] "n"(OFF)
+      : "memory");
+}
+
+template <int VM, int OFF>
+__device__ __forceinline__ void read_stage_d64_dense(const uint32_t (&ka)[2], const uint32_t (&va)[4],
+                                                     f16x8 (&k)[2], f16x4 (&v)[4]) {
+  asm volatile(
+      "s_waitcnt vmcnt(%[vm])\n\t"
+      "ds_read_b128 %[k0], %[ka0] offset:%[off]\n\t"
+      "ds_read_b128 %[k1], %[ka1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v0], %[va0] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v1], %[va1] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v2], %[va2] offset:%[off]\n\t"
+      "ds_read_b64_tr_b16 %[v3], %[va3] offset:%[off]\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [v0] "=&v"(v[0]), [v1] "=&v"(v[1]), [v2] "=&v"(v[2]),
+        [v3] "=&v"(v[3])
+      : [ka0] "v"(ka[0]), [ka1] "v"(ka[1]), [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]),
+        [va3] "v"(va[3]), [vm] "n"(VM), [off] "n"(OFF)
+      : "memory");
+}
+
 template <int D, int VM, int OFF>
 __device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], const uint32_t (&va)[D / 16],
                                               f16x8 (&k)[D / 32], f16x4 (&v)[D / 16], const int32_t* e0,
@@ -1169,8 +1224,10 @@ __device__ __forceinline__ void unroll(F&& f) {
   unroll_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int D, int NST, bool F8>
+// F8: E4M3 pools.  DENSE: the virtually contiguous cache of pa_decode_dense (fp16, no table).
+template <int D, int NST, bool F8, bool DENSE = false>
 __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs a) {
+  static_assert(!(F8 && DENSE), "the contiguous cache is fp16");
   using K = MCfg<D, F8>;
   constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
   constexpr int ROWQ = K::kRowQ, NCQ = K::kNCQ;
@@ -1237,7 +1294,9 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const int r = pos / NC, p = pos % NC;
     const int rr = bsz >= TK ? r : (r & (bsz - 1));  // row within its block
     const int sw = F8 ? swz8<D>(r) : swz(r);
-    lo[i] = static_cast<uint32_t>(rr * ROW + ((p ^ sw) * 16));
+    // contiguous cache: consecutive tokens of one head are token_bytes apart
+    lo[i] = DENSE ? static_cast<uint32_t>(r * a.token_bytes + ((p ^ sw) * 16))
+                  : static_cast<uint32_t>(rr * ROW + ((p ^ sw) * 16));
     hi8[i] = r >= 8;
   }
 
@@ -1273,7 +1332,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     bool bad = false;
     const int kvh = real ? f.unit / a.n_gtiles : 0;
     const int tok0 = f.t * TK;
-    if (real) {
+    if (DENSE) {
+    } else if (real) {
       if (p0 < 0 || p0 >= a.num_blocks) {
         bad = true;
         p0 = 0;
@@ -1304,6 +1364,20 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
                                            16, 0, 0);
         }
       }
+    }
+    if constexpr (DENSE) {  // a tile never leaves the page that holds its first token
+      const int64_t off = static_cast<int64_t>(f.s) * a.seq_bytes + static_cast<int64_t>(tok0) * a.token_bytes +
+                          static_cast<int64_t>(kvh) * ROW;
+      const char* kt = real ? a.dense_k + off : a.guard_k;
+      const char* vt = real ? a.dense_v + off : a.guard_v;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(kt + lo[i]), static_cast<void*>(stage + i * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(vt + lo[i]),
+                                         static_cast<void*>(stage + HALF + i * 1024), 16, 0, 0);
+      }
+      return bad;
     }
     const uint64_t head = static_cast<uint64_t>(kvh) * head_bytes;
     const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
@@ -1478,8 +1552,14 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   // two and three, all the entries come in one batch of scalar loads (one wait).
   Cursor cf = cc;
   const int32_t *e0, *e1;
-  int32_t pe0, pe1;
-  if constexpr (NST == 2) {
+  int32_t pe0 = 0, pe1 = 0;
+  if constexpr (DENSE) {  // no entries: the first NST - 1 tiles straight away
+    unroll<NST - 1>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      fbad[j] = fetch(cf, j < n_my, j < n_my && (j == 0 || cf.t == 0), j, 0, 0);
+      wk.advance(cf);
+    });
+  } else if constexpr (NST == 2) {
     Cursor c1 = cf;
     wk.advance(c1);
     const int32_t *a0, *a1;
@@ -1529,9 +1609,14 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
       const bool real = i + NST - 1 < n_my;
       fbad[nxt] = fetch(cf, real, real && cf.t == 0, nxt, pe0, pe1);
       wk.advance(cf);
-      entry_ptrs(cf, i + NST < n_my, e0, e1);
-      if constexpr (F8) read_stage_f8<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
-      else read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      if constexpr (DENSE) {
+        if constexpr (D == 128) read_stage_d128_dense<VM, st * STAGE>(ka, va, kop, vop);
+        else read_stage_d64_dense<VM, st * STAGE>(ka, va, kop, vop);
+      } else {
+        entry_ptrs(cf, i + NST < n_my, e0, e1);
+        if constexpr (F8) read_stage_f8<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+        else read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      }
       if (i < n_my) process(i, stc);
     });
   }
@@ -2088,6 +2173,7 @@ struct DecodeCall {
   hipStream_t stream;
   bool kv_fp8 = false;  // pools hold E4M3 codes (q and out are fp16)
   float k_scale = 1.0f, v_scale = 1.0f;
+  const pa_vkv* dense = nullptr;  // the virtually contiguous cache instead of pools and tables
 };
 
 int check_decode(const DecodeCall& c, Geom* g) {
@@ -2209,9 +2295,9 @@ int waves_valu(const DecodeCall& c, const Geom& g) {
   return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
 }
 
-template <int D, int NST, bool F8>
+template <int D, int NST, bool F8, bool DENSE>
 int waves_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
-  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8>));
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8, DENSE>));
   int64_t base = static_cast<int64_t>(r.cus) * waves_per_cu;
   if (base > r.waves) base = r.waves;
   return waves_for(c, g, base);
@@ -2247,6 +2333,16 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   a.num_blocks = c.num_blocks;
   a.num_waves = 1;
   a.rec_rows = g.rec_rows;
+  a.dense_k = a.dense_v = a.guard_k = a.guard_v = nullptr;
+  a.seq_bytes = a.token_bytes = 0;
+  if (c.dense) {
+    a.dense_k = c.dense->k_base();
+    a.dense_v = c.dense->v_base();
+    a.guard_k = c.dense->k_reserve;
+    a.guard_v = c.dense->v_reserve;
+    a.seq_bytes = c.dense->seq_bytes;
+    a.token_bytes = c.dense->token_bytes;
+  }
   return a;
 }
 
@@ -2259,11 +2355,11 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
 }
 
 // NST stages, waves_per_cu waves per compute unit
-template <int D, int NST, bool F8>
+template <int D, int NST, bool F8, bool DENSE = false>
 int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
-  a.num_waves = waves_mfma<D, NST, F8>(c, g, waves_per_cu);
-  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  a.num_waves = waves_mfma<D, NST, F8, DENSE>(c, g, waves_per_cu);
+  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_mfma_kernel launch");
 }
 
@@ -2290,6 +2386,7 @@ int dispatch_f32(const DecodeCall& c, const Geom& g) {
 template <int Which, int D>
 int dispatch_f16(const DecodeCall& c, const Geom& g) {
   if (Which == 1) return launch_reduce<f16, D, kMfRows>(c, g);
+  if (c.dense) return launch_stream_mfma<D, kMfStages, false, true>(c, g, kMfWavesPerCU);
   return c.kv_fp8 ? launch_stream_mfma<D, kF8Stages, true>(c, g, kF8WavesPerCU)
                   : launch_stream_mfma<D, kMfStages, false>(c, g, kMfWavesPerCU);
 }
@@ -2577,6 +2674,38 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
   return decode_fp8(1, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
                     block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                     max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_dense(void* out, const void* q, const pa_vkv* kv, float scale, int32_t num_q_heads,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  if (!kv) return fail(PA_ERR_INVALID_ARG, "NULL cache");
+  if (!valid_scale(scale))
+    return fail(PA_ERR_INVALID_ARG, "scale %g must be positive and finite", static_cast<double>(scale));
+  if (num_q_heads <= 0 || num_q_heads % kv->num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_q_heads %d must be a positive multiple of num_kv_heads %d", num_q_heads,
+                kv->num_kv_heads);
+  if (partition_size < 0 || partition_size % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of 16", partition_size);
+  const int32_t num_seqs = kv->num_seqs;
+  if (num_seqs == 0) return PA_OK;
+  const Geom g = geometry(num_seqs, num_q_heads, kv->num_kv_heads, kv->head_dim, kv->max_ctx, partition_size, PA_F16);
+  if (static_cast<int64_t>(num_seqs) * g.n_units * ((static_cast<int64_t>(kv->max_ctx) + 15) / 16) >
+      (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles");
+  if (!out || !q) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned(out, 16) || !aligned(q, 16)) return fail(PA_ERR_INVALID_ARG, "out and q must be 16-byte aligned");
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);
+  if (workspace_bytes < g.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, g.ws_bytes);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  DecodeCall c = make_call(out, q, nullptr, nullptr, nullptr, kv->d_ctx, scale, 16, kv->num_kv_heads, num_seqs,
+                           num_q_heads, kv->head_dim, 0, kv->max_ctx, 0, partition_size, PA_F16, workspace,
+                           workspace_bytes, stream);
+  c.dense = kv;
+  int rc = dispatch<0>(c, g);
+  if (rc != PA_OK) return rc;
+  return dispatch<1>(c, g);
 }
 
 int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 3
+    assert P.lib().pa_abi_version() == (2 << 16) | 4
 
 
 def test_workspace_size_query():
