@@ -62,7 +62,9 @@ def parse():
 ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
                "long_context_b16", "long_context_b32", "llama3_8b_fp8", "llama2_70b_fp8",
                "long_context_b16_fp8", "prefill_llama3_8b", "prefill_llama2_70b",
-               "copy_blocks_device", "swap_out_host"]
+               "copy_blocks_device", "swap_out_host", "paging_tax_llama3_8b",
+               "paging_tax_long_context"]
+PAGING_TAX = ("paging_tax_llama3_8b", "paging_tax_long_context")
 PREFILL = ("prefill_llama3_8b", "prefill_llama2_70b")
 BLOCK_COPIES = ("copy_blocks_device", "swap_out_host")
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, one direction: the host link assumed for swap
@@ -82,6 +84,8 @@ WORKLOAD_NAMES = {
     "prefill_llama2_70b": "whole-prompt prefill, Llama-2-70B shape: 4 prompts of 2048 tokens",
     "copy_blocks_device": "copy-on-write of 4096 blocks within one device pool (8 kv heads x 16 x 128, fp16)",
     "swap_out_host": "swap out of 1024 blocks from the device pools to pinned host pools (8 x 16 x 128, fp16)",
+    "paging_tax_llama3_8b": "paged vs virtually contiguous decode, Llama-3-8B-shaped layer",
+    "paging_tax_long_context": "paged vs virtually contiguous decode, 32K-128K contexts, block size 16",
 }
 FP8_SUFFIX = "_fp8"
 
@@ -184,6 +188,8 @@ def main():
             result = run_prefill(args, name)
         elif name in BLOCK_COPIES:
             result = run_block_copies(args, name)
+        elif name in PAGING_TAX:
+            result = run_paging_tax(args, name)
         else:
             result = run_one(args, name)
         print(json.dumps(result), flush=True)
@@ -577,6 +583,107 @@ def run_block_copies(args, config):
         result["cpu_baseline"] = {"value": round(2 * len(sub) * block_bytes / dt / 1e9, 3), "unit": "GB/s",
                                   "cores": 1, "kind": "oracle",
                                   "sample": f"{len(sub)} block pairs within a {n_pool // 4}-block host pool"}
+    return result
+
+
+def run_paging_tax(args, config):
+    """The same decode over the same tokens, once through block tables over a scattered pool
+    (pa_decode) and once over a virtually contiguous cache backed page by page through HIP
+    virtual memory (pa_decode_dense): the paging tax is the time difference."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_167_amd as P
+    import workloads as W
+    dev = torch.device("cuda:0")
+    case = W.llama3_8b() if config == "paging_tax_llama3_8b" else W.long_context(16)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)  # noqa: E731
+    q, tables, ctx = t(case.q), t(case.block_tables), t(case.context_lens)
+    shape = (case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim)
+    kc = torch.full(shape, float("nan"), dtype=torch.float16, device=dev)
+    vc = torch.full(shape, float("nan"), dtype=torch.float16, device=dev)
+    P.pa_cache_write(t(case.prefix_k), t(case.prefix_v), t(case.prefix_slots), kc, vc)
+    P.pa_cache_write(t(case.new_k), t(case.new_v), t(case.new_slots), kc, vc)
+    mcl = case.max_context_len
+    out_p, out_d = torch.empty_like(q), torch.empty_like(q)
+    ws = torch.empty(P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
+                                                 case.head_dim, mcl, 0), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        hot = e0.elapsed_time(e1) / args.steps
+        cold = []
+        for _ in range(5):
+            flush.sum()
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            cold.append(e0.elapsed_time(e1))
+        return hot, float(np.median(cold))
+
+    ph, pc = timed(lambda: P.pa_decode(out_p, q, kc, vc, tables, ctx, case.scale, case.block_size,
+                                       case.num_kv_heads, max_context_len=mcl, workspace=ws, stream=stream))
+    seq = np.concatenate([np.full(int(c) - 1, s, np.int32) for s, c in enumerate(case.context_lens)])
+    pos = np.concatenate([np.arange(int(c) - 1, dtype=np.int32) for c in case.context_lens])
+    order = np.concatenate(case.meta["seq_rows"])
+    dense = {}
+    token_bytes = case.num_kv_heads * case.head_dim * 2
+    for want in (256 << 10, 2 << 20, 8 << 20):  # page sizes, rounded up to whole 16-token tiles
+        unit = 16 * token_bytes
+        page = -(-want // unit) * unit
+        try:
+            kv = P.DenseKV(case.num_seqs, mcl, case.num_kv_heads, case.head_dim, page_bytes=page)
+        except P.PaError as err:  # not a multiple of the allocation granularity
+            dense[f"{page >> 10}K"] = {"error": str(err)}
+            continue
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        try:
+            kv.step(case.context_lens.tolist())  # every page mapped from scratch
+        except P.PaError as err:
+            dense[f"{page >> 10}K"] = {"error": str(err)}
+            kv.close()
+            continue
+        map_ms = (time.perf_counter() - t0) * 1e3
+        pages = kv.mapped_bytes // kv.page_bytes
+        kv.write(t(case.prefix_k[order]), t(case.prefix_v[order]), t(seq), t(pos))
+        kv.write(t(case.new_k), t(case.new_v), t(np.arange(case.num_seqs, dtype=np.int32)),
+                 t((case.context_lens - 1).astype(np.int32)))
+        dh, dc = timed(lambda: kv.decode(out_d, q, case.scale, workspace=ws, stream=stream))
+        dense[f"{kv.page_bytes >> 10}K"] = {
+            "us": round(dh * 1e3, 2), "cold_us": round(dc * 1e3, 2),
+            "kv_gbs": round(case.kv_bytes() / (dh * 1e-3) / 1e9, 1), "pages_mapped": int(pages),
+            "map_all_ms": round(map_ms, 3), "map_us_per_page": round(map_ms * 1e3 / max(pages, 1), 2),
+            "paging_tax_pct": round(100.0 * (ph / dh - 1.0), 2),
+            "outputs_bitwise_equal": bool(torch.equal(out_p, out_d))}
+        kv.close()
+    kv_bytes = case.kv_bytes()
+    best = min((v["us"], k) for k, v in dense.items() if "us" in v) if any("us" in v for v in dense.values()) \
+        else (float("nan"), None)
+    dh = best[0] * 1e-3
+    result = {
+        "metric": "paging tax: pa_decode over block tables vs over a virtually contiguous cache",
+        "value": round(100.0 * (ph / dh - 1.0), 2), "unit": "% slower paged than the best page size (warm)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ph, 5),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[config], "name": config, "num_seqs": case.num_seqs,
+                   "kv_bytes_per_step": kv_bytes, "block_size": case.block_size},
+        "paged": {"us": round(ph * 1e3, 2), "cold_us": round(pc * 1e3, 2),
+                  "kv_gbs": round(kv_bytes / (ph * 1e-3) / 1e9, 1)},
+        "dense_by_page_size": dense, "best_page": best[1],
+    }
     return result
 
 

@@ -318,9 +318,10 @@ int pa_allocator_move(pa_allocator* src, pa_allocator* dst, int32_t* tables, con
  *
  * pa_vkv_create -- reserve K and V address ranges for max_seqs sequences of up to
  *   max_context_len tokens, laid out [max_seqs][region][num_kv_heads][head_dim] with each
- *   sequence's region a whole number of pages.  page_bytes 0 picks the smallest page that
- *   is a multiple of the allocation granularity and of 16 tokens; otherwise it must be such a
- *   multiple.  Returns NULL on error (see pa_last_error).  Allocates device memory.
+ *   sequence's region a whole number of pages.  Pages are multiples of the allocation
+ *   granularity and of 16 tokens; page_bytes 0 picks the smallest such page of at least
+ *   2 MB, otherwise page_bytes must be such a multiple.  Returns NULL on error (see
+ *   pa_last_error).  Allocates device memory.
  * pa_vkv_step -- before an iteration: map pages so that tokens [0, context_lens[s]) of every
  *   sequence s < num_seqs are backed (never unmaps), and record the lengths (host array) for
  *   pa_decode_dense.  Synchronises the stream.  PA_ERR_EXHAUSTED when memory runs out; the
