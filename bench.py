@@ -452,6 +452,12 @@ def run_prefill(args, config):
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     mql, mcl = case.max_query_len, case.max_context_len
+    if args.calibrate_copy_mib > 0:  # a copy of known size that scales the HBM byte counters
+        src = torch.ones(args.calibrate_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def write_only():
         P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
@@ -502,7 +508,8 @@ def run_prefill(args, config):
         "pa_cache_write": {"us": round(per["write"] * 1e3, 2)},
         "roofline": {"kernel": "pa_prefill_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("pa_prefill_kernel", config, 0),  # HBM bytes per launch
                      "alg_flops_per_launch": flops, "avg_launch_us": round(per["prefill"] * 1e3, 2)},
     }
     if not args.no_cpu_baseline:
