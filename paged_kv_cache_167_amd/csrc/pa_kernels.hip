@@ -1645,7 +1645,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 constexpr int kPfWaves = 4;                            // waves per work-group
 constexpr int kPfInterleave = 2;                       // blocks whose score products interleave
 constexpr int kPfKeys = 32;                            // keys per tile
-constexpr int kPfStages = 3;
+constexpr int kPfStages = 2;
+constexpr int kPfBlocks = 2;  // 16-row product blocks per wave: 32 query rows
 
 struct PrefillArgs {
   void* out;
@@ -1767,7 +1768,7 @@ __device__ __forceinline__ void pf_read_d64(const uint32_t (&ka)[2], const uint3
 
 // NR 16-row product blocks per wave, an NST-stage ring
 template <int D, int NR, int NST>
-__global__ __launch_bounds__(kPfWaves * kWave) void pa_prefill_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const PrefillArgs a) {
   using C = PCfg<D>;
   constexpr int ROW = C::kRow, NC = C::kNC, TILE = C::kTile, STAGE = C::kStage;
   constexpr int LOADS = C::kLoads, KB = C::kKB, NB = C::kNB;
@@ -2438,15 +2439,13 @@ int launch_prefill_rows(PrefillArgs a, int64_t rows, int num_seqs, hipStream_t s
   return check_hip("pa_prefill_kernel launch");
 }
 
-// Rows per wave: 64 (four 16-row blocks, one wave per SIMD) serve each K/V tile to the most
-// rows and were fastest for chunks after a long cached prefix; 16 (two waves per SIMD, more
-// and shorter work-groups) were fastest where the chunks make up most of the context, the
-// causal triangle of whole prompts.  Measured on MI355X; chosen from the host bounds.
+// 32 rows per wave (two 16-row blocks) with the kernel held to 256 registers, so that two
+// waves share each SIMD and one's softmax runs beside the other's products, and a 2-stage
+// ring: measured fastest on MI355X both for chunks after a long cached prefix and for whole
+// prompts (64 rows per wave needs more registers and runs one wave per SIMD).
 template <int D>
 int launch_prefill(const PrefillArgs& a, int64_t rows, int num_seqs, hipStream_t stream) {
-  if (2 * static_cast<int64_t>(a.max_query_len) >= a.max_context_len)
-    return launch_prefill_rows<D, 1>(a, rows, num_seqs, stream);
-  return launch_prefill_rows<D, 4>(a, rows, num_seqs, stream);
+  return launch_prefill_rows<D, kPfBlocks>(a, rows, num_seqs, stream);
 }
 
 DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* v_cache,
