@@ -44,7 +44,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 10; 200 for the prefill workloads, whose "
+                         "launch times keep drifting while the clocks settle under matrix load)")
     ap.add_argument("--config", default="llama3_8b", choices=ALL_CONFIGS + ["all"],
                     help="workload; 'all' runs every one in turn, one JSON line each")
     ap.add_argument("--partition", type=int, default=0,
@@ -56,7 +58,9 @@ def parse():
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic that scales the HBM byte counters)")
-    return ap.parse_args()
+    args = ap.parse_args()
+    args.warmup_arg = args.warmup
+    return args
 
 
 ALL_CONFIGS = ["tiny_fp32", "llama3_8b", "llama2_70b", "shared_prefix", "long_context_b8",
@@ -68,6 +72,7 @@ PAGING_TAX = ("paging_tax_llama3_8b", "paging_tax_long_context")
 PREFILL = ("prefill_llama3_8b", "prefill_llama2_70b")
 BLOCK_COPIES = ("copy_blocks_device", "swap_out_host")
 HOST_LINK_GBS = 64.0  # PCIe 5.0 x16, one direction: the host link assumed for swap
+PREFILL_WARMUP = 200  # ~50 ms of matrix work: launch times settle within about 100 launches
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix peak, published
 WORKLOAD_NAMES = {
     "tiny_fp32": "tiny fp32 decode (4 sequences, ctx 1..250)",
@@ -184,6 +189,9 @@ def main():
     import workloads
     workloads.set_progress(log)
     for name in (ALL_CONFIGS if args.config == "all" else [args.config]):
+        args = argparse.Namespace(**{**vars(args), "warmup": args.warmup_arg})
+        if args.warmup is None:
+            args.warmup = PREFILL_WARMUP if name in PREFILL else 10
         if name in PREFILL:
             result = run_prefill(args, name)
         elif name in BLOCK_COPIES:

@@ -1630,9 +1630,9 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 //
 // One work-group of four waves per (query-row block, kv head, sequence).  The rows of a
 // (sequence, kv head) are its chunk tokens times the G query heads of the group, token
-// major; a work-group takes 256 of them (64 per wave, four 16-row product blocks), so
-// every K/V tile it brings into LDS serves 256 rows.  The tiles hold 32 keys and pass
-// through a 3-stage ring that the four waves fill together (each loads 8 key rows, which
+// major; a work-group takes 16 * NR of them per wave (NR 16-row product blocks), and every
+// K/V tile it brings into LDS serves all of its rows.  The tiles hold 32 keys and pass
+// through an NST-stage ring that the four waves fill together (each loads 8 key rows, which
 // lie in one block for block sizes 8, 16 and 32) and read after a barrier.  Per tile and
 // 16-row block: scores S^T = K Q^T with two 16x16x32 products per 32 dims (one per key
 // half), and O^T += V^T P^T with one 16x16x32 product per 16 dims, its 32 keys in the

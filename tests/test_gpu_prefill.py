@@ -93,7 +93,7 @@ SMALL = [
     (64, 8, 16, 1, [130, 40], [66, 40]),
     (128, 16, 16, 1, [300, 33], [31, 33]),
     (64, 32, 6, 2, [1024], [300]),
-    # chunks that are most of their context (whole prompts): the 16-rows-per-wave variant
+    # chunks that are most of their context (whole prompts)
     (128, 16, 8, 2, [300, 64, 1, 130], [300, 64, 1, 100]),
     (64, 8, 28, 4, [200, 17], [150, 17]),
     (128, 32, 16, 2, [257], [257]),
