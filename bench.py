@@ -1,9 +1,12 @@
 #!/usr/bin/env python3
 """Paged decode benchmark on one MI355X.
 
-One step = the whole hot path over one batch: pa_cache_write of every
-sequence's new token, then pa_decode (the stream kernel, whose persistent waves
-each take an equal share of the batch's tiles, then the log-sum-exp reduce).
+One step = the whole hot path over one batch: store every sequence's new token
+in its last block, then attend over the whole context.  For fp16 pools that is one
+pa_decode_append (the stream kernel, whose persistent waves each take an equal share
+of the batch's tiles and read the new tokens from their input rows, then the
+log-sum-exp reduce, which also stores the new tokens); for E4M3 and fp32 pools it is
+pa_cache_write (or pa_cache_write_fp8), then pa_decode (or pa_decode_fp8).
 Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
 heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
 blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.
@@ -43,7 +46,8 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    # 200 back-to-back steps: the host's start and stop latency is under 1 % of the timed span
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed warm-up steps (default 10; 200 for the prefill workloads, whose "
                          "launch times keep drifting while the clocks settle under matrix load)")
@@ -239,6 +243,15 @@ def run_one(args, config):
     new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
     out = torch.empty_like(q)
     mcl = case.max_context_len
+    # fp16 pools: the step is one pa_decode_append, which stores each new token at the slot
+    # its table gives position ctx - 1 (the workloads put it exactly there) and attends
+    fused = not fp8 and case.dtype == np.float16
+    if fused:
+        last = case.context_lens.astype(np.int64) - 1
+        table_slots = case.block_tables[np.arange(case.num_seqs), last // case.block_size].astype(np.int64) * \
+            case.block_size + last % case.block_size
+        assert np.array_equal(table_slots, case.new_slots), "new tokens off their table slots"
+
     ws_bytes = P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                            case.head_dim, mcl, partition)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -259,7 +272,11 @@ def run_one(args, config):
             P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
 
     def decode_only():
-        if fp8:
+        if fused:
+            P.pa_decode_append(out, q, new_k, new_v, k_cache, v_cache, tables, ctx, case.scale,
+                               case.block_size, case.num_kv_heads, max_context_len=mcl,
+                               partition_size=partition, workspace=ws, stream=stream)
+        elif fp8:
             P.pa_decode_fp8(out, q, k_cache, v_cache, tables, ctx, case.scale, k_scale, v_scale,
                             case.block_size, case.num_kv_heads, max_context_len=mcl,
                             partition_size=partition, workspace=ws, stream=stream)
@@ -269,11 +286,17 @@ def run_one(args, config):
                         workspace=ws, stream=stream)
 
     def step():
-        write_only()
+        if not fused:
+            write_only()
         decode_only()
 
-    def stream_kernel():  # the first of pa_decode's two launches, on its own
-        if fp8:
+    def stream_kernel():  # the first of the step's two attention launches, on its own
+        if fused:
+            P.pa_decode_append_partitions(out, q, new_k, new_v, k_cache, v_cache, tables, ctx,
+                                          case.scale, case.block_size, case.num_kv_heads,
+                                          max_context_len=mcl, partition_size=partition,
+                                          workspace=ws, stream=stream)
+        elif fp8:
             P.pa_decode_fp8_partitions(out, q, k_cache, v_cache, tables, ctx, case.scale, k_scale,
                                        v_scale, case.block_size, case.num_kv_heads,
                                        max_context_len=mcl, partition_size=partition,
@@ -371,10 +394,13 @@ def run_one(args, config):
                             f"sum {int(case.context_lens.sum())}",
             "partition_size": partition, "kv_bytes_per_step": kv_bytes,
             "kv_cache": "e4m3" if fp8 else ("f16" if case.dtype == np.float16 else "f32"),
+            "step": "pa_decode_append" if fused else
+                    ("pa_cache_write_fp8 + pa_decode_fp8" if fp8 else "pa_cache_write + pa_decode"),
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "pa_decode": {
+            "call": "pa_decode_append" if fused else ("pa_decode_fp8" if fp8 else "pa_decode"),
             "us": round(per_call_ms["decode"] * 1e3, 2),
             "kv_gbs": round(kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
@@ -382,7 +408,8 @@ def run_one(args, config):
             "unique_kv_gbs": round(unique / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
             "seqs_per_s_per_layer": round(case.num_seqs / (per_call_ms["decode"] * 1e-3), 1),
         },
-        "pa_cache_write": {
+        "pa_cache_write": {  # with pa_decode_append the step does not call it: timed alone
+            "in_step": not fused,
             "us": round(per_call_ms["write"] * 1e3, 2),
             "gbs": round(write_bytes / (per_call_ms["write"] * 1e-3) / 1e9, 2),
             "bytes": write_bytes,

@@ -164,6 +164,47 @@ int pa_decode_reduce(void* out, const int32_t* context_lens,
                      const void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_append -- one decode step in one call: store each sequence's new token and
+ * attend over its whole context, the token included ([SRC] section 3.2 appends the token
+ * into the sequence's last block; [SOSP] section 3.4 writes it, then attends over every
+ * valid position).
+ *
+ * The new token of sequence s is position p = context_lens[s] - 1; its rows k_new[s], v_new[s]
+ * are stored at (block_tables[s, p / block_size], p % block_size) of the pools, the slot
+ * that position has in the table, and out is what pa_decode gives after that store.  The
+ * results equal pa_cache_write (with that slot for each sequence) followed by pa_decode,
+ * bit for bit.  Fewer launches: the attention kernel takes the new token from k_new / v_new
+ * rather than the pools, and the second launch (which merges split contexts) stores it.
+ * fp16 only (q, k_new, v_new, pools and out), with pa_decode's sizes, workspace, checks and
+ * results; sequences with an empty or invalid context, or whose table entry for p lies
+ * outside the pool, store nothing.  As with pa_cache_write, two sequences whose new tokens
+ * share a slot race, and the caller must not store into a block other tables still read
+ * (copy it first, see pa_allocator_append_slot).
+ *
+ * k_new, v_new   device, [num_seqs, num_kv_heads, head_dim] fp16, 16-byte aligned
+ * k_cache, v_cache  updated in place at one slot per sequence
+ * other arguments as for pa_decode (dtype is PA_F16)
+ *
+ * pa_decode_append_partitions -- the first of the two launches alone (attention pieces,
+ * new tokens read from k_new / v_new; nothing is stored): pa_decode_reduce merges its
+ * pieces, but only pa_decode_append stores the new tokens.
+ */
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                     void* k_cache, void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, float scale, int32_t block_size,
+                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream);
+
+int pa_decode_append_partitions(void* out, const void* q, const void* k_new, const void* v_new,
+                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, int32_t block_size,
+                                int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int64_t num_blocks, int32_t partition_size,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * FP8 KV cache ([CON] section 6: blocks store K/V compressed, the kernel expands them).
  *
  * The pages name FP8 but no format or scaling; these calls take the OCP E4M3 format
@@ -358,7 +399,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 4)
+#define PA_ABI_VERSION ((2 << 16) | 5)
 
 #ifdef __cplusplus
 }

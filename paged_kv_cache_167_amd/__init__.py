@@ -16,6 +16,8 @@ from ._lib import (  # noqa: F401
     pa_copy_blocks,
     pa_cache_write_fp8,
     pa_decode,
+    pa_decode_append,
+    pa_decode_append_partitions,
     pa_decode_fp8,
     pa_decode_fp8_partitions,
     pa_decode_partitions,

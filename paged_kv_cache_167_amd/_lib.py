@@ -44,6 +44,13 @@ SIGNATURES = {
                                         _c_int64, _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
     "pa_decode_reduce": (_c_int32, [_vp, _vp, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                     _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_append": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32,
+                                    _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                    _c_int64, _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_append_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                               _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                               _c_int32, _c_int32, _c_int64, _c_int32, _vp,
+                                               ctypes.c_size_t, _vp]),
     "pa_cache_write_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
                                       _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
     "pa_decode_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
@@ -214,6 +221,43 @@ def pa_decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition
                                   int(partition_size), _dtype_code(out), ws_ptr, ws_bytes,
                                   _stream(out, stream))
     _check("pa_decode_reduce", code)
+
+
+def _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                        block_size, num_kv_heads, max_context_len, partition_size, workspace, stream):
+    import torch
+    if q.dtype != torch.float16 or k_cache.dtype != torch.float16:
+        raise PaError("binding", PA_ERR_UNSUPPORTED, "pa_decode_append takes float16 tensors")
+    if k_new.shape != (q.shape[0], k_cache.shape[1], q.shape[2]) or v_new.shape != k_new.shape:
+        raise PaError("binding", PA_ERR_INVALID_ARG, "k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    args, workspace = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   block_size, num_kv_heads, max_context_len, partition_size,
+                                   workspace, stream)
+    # (out, q, k_new, v_new, kc, vc, bt, ctx, scale, block_size, ...) without the dtype
+    return args[:2] + (_ptr(k_new), _ptr(v_new)) + args[2:16] + args[17:], workspace
+
+
+def pa_decode_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                     block_size, num_kv_heads, max_context_len=None,
+                     partition_size=DEFAULT_PARTITION, workspace=None, stream=None):
+    """One decode step: store k_new[s], v_new[s] at position context_lens[s] - 1 of each
+    sequence (the slot its table gives) and attend over the whole context (fp16)."""
+    args, workspace = _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                          context_lens, scale, block_size, num_kv_heads,
+                                          max_context_len, partition_size, workspace, stream)
+    _check("pa_decode_append", lib().pa_decode_append(*args))
+    return workspace
+
+
+def pa_decode_append_partitions(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                scale, block_size, num_kv_heads, max_context_len=None,
+                                partition_size=DEFAULT_PARTITION, workspace=None, stream=None):
+    """First launch of pa_decode_append alone (stores nothing); pa_decode_reduce merges."""
+    args, workspace = _decode_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                          context_lens, scale, block_size, num_kv_heads,
+                                          max_context_len, partition_size, workspace, stream)
+    _check("pa_decode_append_partitions", lib().pa_decode_append_partitions(*args))
+    return workspace
 
 
 def _require_codes(t, name):

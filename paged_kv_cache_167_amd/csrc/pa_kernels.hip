@@ -415,6 +415,23 @@ struct StreamArgs {
   const char* guard_v;
   int64_t seq_bytes;
   int64_t token_bytes;
+  // append mode: the token at position ctx - 1 of sequence s is read from these rows
+  // ([num_seqs, num_kv_heads, head_dim]) instead of the pools
+  const char* k_new;
+  const char* v_new;
+};
+
+// Append mode of the reduce kernel: where the new tokens' rows go (k_new == nullptr: off).
+struct AppendArgs {
+  const u32x4* k_new;  // [num_seqs, num_kv_heads, head_dim] rows, in 16-byte chunks
+  const u32x4* v_new;
+  u32x4* k_cache;  // the pools
+  u32x4* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  int block_size;
+  int num_kv_heads;
+  int64_t num_blocks;
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -1225,9 +1242,12 @@ __device__ __forceinline__ void unroll(F&& f) {
 }
 
 // F8: E4M3 pools.  DENSE: the virtually contiguous cache of pa_decode_dense (fp16, no table).
-template <int D, int NST, bool F8, bool DENSE = false>
+// APPEND: each sequence's newest token (position ctx - 1) comes from a.k_new / a.v_new, not
+// from the pools, which the same call writes only after this kernel (pa_decode_append).
+template <int D, int NST, bool F8, bool DENSE = false, bool APPEND = false>
 __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs a) {
   static_assert(!(F8 && DENSE), "the contiguous cache is fp16");
+  static_assert(!APPEND || (!F8 && !DENSE), "append mode reads fp16 pools");
   using K = MCfg<D, F8>;
   constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
   constexpr int ROWQ = K::kRowQ, NCQ = K::kNCQ;
@@ -1288,12 +1308,16 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   const int bsz = a.block_size;
   uint32_t lo[LOADS];
   bool hi8[LOADS];
+  int row_of[LOADS];         // append mode: the tile row of load i, and the offset of its
+  uint32_t chunk_of[LOADS];  // chunk within a row
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pos = i * 64 + lane;
     const int r = pos / NC, p = pos % NC;
     const int rr = bsz >= TK ? r : (r & (bsz - 1));  // row within its block
     const int sw = F8 ? swz8<D>(r) : swz(r);
+    row_of[i] = r;
+    chunk_of[i] = static_cast<uint32_t>((p ^ sw) * 16);
     // contiguous cache: consecutive tokens of one head are token_bytes apart
     lo[i] = DENSE ? static_cast<uint32_t>(r * a.token_bytes + ((p ^ sw) * 16))
                   : static_cast<uint32_t>(rr * ROW + ((p ^ sw) * 16));
@@ -1383,6 +1407,27 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
                         static_cast<uint64_t>(tok0 & (bsz - 1)) * ROW;
     const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
+    if constexpr (APPEND) {
+      if (real && tok0 + TK >= f.ctx) {  // the context's last tile: row ctx - 1 - tok0 is new
+        const int rn = f.ctx - 1 - tok0;
+        const int64_t nrow = (static_cast<int64_t>(f.s) * a.num_kv_heads + kvh) * ROW;
+        const char* kn = a.k_new + nrow;
+        const char* vn = a.v_new + nrow;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+          const bool second = bsz < TK && (K::kRowsPerLoad > 8 ? hi8[i] : i * K::kRowsPerLoad >= 8);
+          const uint64_t off = (second ? b1 : b0) + lo[i];
+          const bool mine = row_of[i] == rn;
+          const char* kp = mine ? kn + chunk_of[i] : kcache + off;
+          const char* vp = mine ? vn + chunk_of[i] : vcache + off;
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(kp), static_cast<void*>(stage + i * 1024), 16,
+                                           0, 0);
+          __builtin_amdgcn_global_load_lds(static_cast<const void*>(vp),
+                                           static_cast<void*>(stage + HALF + i * 1024), 16, 0, 0);
+        }
+        return bad;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       // wave-uniform unless one load spans both halves (16 rows of 64 codes)
@@ -2056,7 +2101,7 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
     T* __restrict__ out, const int2* __restrict__ seg_desc, const float* __restrict__ rec_m,
     const float* __restrict__ rec_l, const float* __restrict__ rec_o,
     const int32_t* __restrict__ context_lens, int num_q_heads, int group, int n_gtiles,
-    int max_context_len, int w_cap, int rec_rows) {
+    int max_context_len, int w_cap, int rec_rows, const AppendArgs ap) {
   constexpr int kDPL = D / kWave;  // dims per lane
   const int h = blockIdx.x;
   const int s = blockIdx.y;
@@ -2068,6 +2113,22 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
   const int n_units = (num_q_heads / group) * n_gtiles;
   const int ctx = context_lens[s];  // both loads in flight together
   const int2 d = seg_desc[s * n_units + kvh * n_gtiles + gtile];
+  if (ap.k_new != nullptr && h == kvh * group && ctx >= 1 && ctx <= max_context_len) {
+    // append mode: the first query head of each kv head stores the new token's K and V
+    // rows at position ctx - 1 (the stream kernel read them from k_new / v_new)
+    constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
+    static_assert(2 * kChunks <= kWave, "one lane per chunk of the K and V rows");
+    const int64_t blk = ap.block_tables[static_cast<int64_t>(s) * ap.max_blocks_per_seq +
+                                        (ctx - 1) / ap.block_size];
+    if (blk >= 0 && blk < ap.num_blocks && lane < 2 * kChunks) {
+      const int c = lane % kChunks;
+      const int64_t row = (static_cast<int64_t>(s) * ap.num_kv_heads + kvh) * kChunks + c;
+      const int64_t slot = ((blk * ap.num_kv_heads + kvh) * ap.block_size + (ctx - 1) % ap.block_size) *
+                               kChunks + c;
+      if (lane < kChunks) ap.k_cache[slot] = ap.k_new[row];
+      else ap.v_cache[slot] = ap.v_new[row];
+    }
+  }
   if (ctx <= 0 || ctx > max_context_len) {  // nothing to attend over: zeros; invalid: NaN
     const T fill = static_cast<T>(ctx == 0 ? 0.0f : __builtin_nanf(""));
 #pragma unroll
@@ -2175,6 +2236,8 @@ struct DecodeCall {
   bool kv_fp8 = false;  // pools hold E4M3 codes (q and out are fp16)
   float k_scale = 1.0f, v_scale = 1.0f;
   const pa_vkv* dense = nullptr;  // the virtually contiguous cache instead of pools and tables
+  const void* k_new = nullptr;    // append mode: the new tokens' K and V rows
+  const void* v_new = nullptr;
 };
 
 int check_decode(const DecodeCall& c, Geom* g) {
@@ -2219,6 +2282,11 @@ int check_decode(const DecodeCall& c, Geom* g) {
   if (c.workspace_bytes < g->ws_bytes)
     return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.workspace_bytes, g->ws_bytes);
   if (!aligned(c.workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (c.k_new || c.v_new) {
+    if (!c.k_new || !c.v_new) return fail(PA_ERR_INVALID_ARG, "k_new or v_new is NULL");
+    if (!aligned(c.k_new, 16) || !aligned(c.v_new, 16))
+      return fail(PA_ERR_INVALID_ARG, "k_new and v_new must be 16-byte aligned");
+  }
   return PA_OK;
 }
 
@@ -2296,9 +2364,9 @@ int waves_valu(const DecodeCall& c, const Geom& g) {
   return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
 }
 
-template <int D, int NST, bool F8, bool DENSE>
+template <int D, int NST, bool F8, bool DENSE, bool APPEND>
 int waves_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
-  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8, DENSE>));
+  const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>));
   int64_t base = static_cast<int64_t>(r.cus) * waves_per_cu;
   if (base > r.waves) base = r.waves;
   return waves_for(c, g, base);
@@ -2344,6 +2412,8 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
     a.seq_bytes = c.dense->seq_bytes;
     a.token_bytes = c.dense->token_bytes;
   }
+  a.k_new = static_cast<const char*>(c.k_new);
+  a.v_new = static_cast<const char*>(c.v_new);
   return a;
 }
 
@@ -2356,21 +2426,34 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
 }
 
 // NST stages, waves_per_cu waves per compute unit
-template <int D, int NST, bool F8, bool DENSE = false>
+template <int D, int NST, bool F8, bool DENSE = false, bool APPEND = false>
 int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
-  a.num_waves = waves_mfma<D, NST, F8, DENSE>(c, g, waves_per_cu);
-  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
+  a.num_waves = waves_mfma<D, NST, F8, DENSE, APPEND>(c, g, waves_per_cu);
+  hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>), dim3(a.num_waves), dim3(kWave), 0, c.stream,
+                     a);
   return check_hip("pa_stream_mfma_kernel launch");
 }
 
 template <typename T, int D, int GT>
 int launch_reduce(const DecodeCall& c, const Geom& g) {
   const WsParts ws = split_workspace(c.workspace, g);
+  AppendArgs ap{};  // k_new == nullptr: the reduce writes no cache row
+  if (c.k_new) {
+    ap.k_new = static_cast<const u32x4*>(c.k_new);
+    ap.v_new = static_cast<const u32x4*>(c.v_new);
+    ap.k_cache = static_cast<u32x4*>(const_cast<void*>(c.k_cache));
+    ap.v_cache = static_cast<u32x4*>(const_cast<void*>(c.v_cache));
+    ap.block_tables = c.block_tables;
+    ap.max_blocks_per_seq = c.max_blocks_per_seq;
+    ap.block_size = c.block_size;
+    ap.num_kv_heads = c.num_kv_heads;
+    ap.num_blocks = c.num_blocks;
+  }
   hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
                      c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
                      c.context_lens, c.num_q_heads, c.num_q_heads / c.num_kv_heads, g.n_gtiles,
-                     c.max_context_len, g.w_cap, g.rec_rows);
+                     c.max_context_len, g.w_cap, g.rec_rows, ap);
   return check_hip("pa_reduce_kernel launch");
 }
 
@@ -2388,6 +2471,7 @@ template <int Which, int D>
 int dispatch_f16(const DecodeCall& c, const Geom& g) {
   if (Which == 1) return launch_reduce<f16, D, kMfRows>(c, g);
   if (c.dense) return launch_stream_mfma<D, kMfStages, false, true>(c, g, kMfWavesPerCU);
+  if (c.k_new) return launch_stream_mfma<D, kMfStages, false, false, true>(c, g, kMfWavesPerCU);
   return c.kv_fp8 ? launch_stream_mfma<D, kF8Stages, true>(c, g, kF8WavesPerCU)
                   : launch_stream_mfma<D, kMfStages, false>(c, g, kMfWavesPerCU);
 }
@@ -2595,6 +2679,51 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   rc = dispatch<0>(c, g);
   if (rc != PA_OK) return rc;
   return dispatch<1>(c, g);
+}
+
+static int decode_append(int launches, void* out, const void* q, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, int32_t block_size, int32_t num_kv_heads,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  DecodeCall c = make_call(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                           num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                           max_context_len, num_blocks, partition_size, PA_F16, workspace, workspace_bytes,
+                           stream);
+  c.k_new = k_new;
+  c.v_new = v_new;
+  if (num_seqs > 0 && (!k_new || !v_new)) return fail(PA_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  Geom g;
+  int rc = check_decode(c, &g);
+  if (rc != PA_OK) return rc;
+  rc = dispatch<0>(c, g);
+  if (rc != PA_OK || launches == 1) return rc;
+  return dispatch<1>(c, g);
+}
+
+int pa_decode_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                     void* v_cache, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                     int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                     int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_append(2, out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq, max_context_len,
+                       num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_append_partitions(void* out, const void* q, const void* k_new, const void* v_new,
+                                const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                const int32_t* context_lens, float scale, int32_t block_size,
+                                int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                                int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_append(1, out, q, k_new, v_new, const_cast<void*>(k_cache), const_cast<void*>(v_cache),
+                       block_tables, context_lens, scale, block_size, num_kv_heads, num_seqs, num_q_heads,
+                       head_dim, max_blocks_per_seq, max_context_len, num_blocks, partition_size, workspace,
+                       workspace_bytes, stream);
 }
 
 int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping, void* k_cache,
