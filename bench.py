@@ -3,10 +3,10 @@
 
 One step = the whole hot path over one batch: store every sequence's new token
 in its last block, then attend over the whole context.  For fp16 pools that is one
-pa_decode_append (the stream kernel, whose persistent waves each take an equal share
-of the batch's tiles and read the new tokens from their input rows, then the
-log-sum-exp reduce, which also stores the new tokens); for E4M3 and fp32 pools it is
-pa_cache_write (or pa_cache_write_fp8), then pa_decode (or pa_decode_fp8).
+pa_decode_append (the stream kernel, whose persistent waves each take an equal share of
+the batch's tiles and take the new tokens from their input rows, then the log-sum-exp
+reduce, which also stores the new tokens); for E4M3 and fp32 pools it is
+pa_cache_write(_fp8), then pa_decode(_fp8) (--step chooses).
 Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
 heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
 blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.
@@ -59,6 +59,14 @@ def parse():
     ap.add_argument("--cold-iters", type=int, default=10,
                     help="extra stream-kernel launches each after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode workloads: replay one captured HIP graph of the step instead of "
+                         "launching every timed step from the host (slower on ROCm 7)")
+    ap.add_argument("--step", choices=["auto", "fused", "unfused"], default="auto",
+                    help="decode workloads: 'fused' = one pa_decode_append (pa_decode_fp8_append) "
+                         "per step; 'unfused' = pa_cache_write(_fp8), then pa_decode(_fp8); 'auto' = "
+                         "fused for fp16 pools and unfused for E4M3 (and fp32) pools, the faster "
+                         "form of each on MI355X")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic that scales the HBM byte counters)")
@@ -243,9 +251,11 @@ def run_one(args, config):
     new_k, new_v, new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
     out = torch.empty_like(q)
     mcl = case.max_context_len
-    # fp16 pools: the step is one pa_decode_append, which stores each new token at the slot
-    # its table gives position ctx - 1 (the workloads put it exactly there) and attends
-    fused = not fp8 and case.dtype == np.float16
+    # fused step: one pa_decode_append (pa_decode_fp8_append), which stores each new token at
+    # the slot its table gives position ctx - 1 (the workloads put it exactly there) and
+    # attends.  By default for fp16 pools only: for E4M3 pools the fused stream kernel's
+    # operand substitution costs as much as the separate store launch saves.
+    fused = case.dtype == np.float16 and (args.step == "fused" or (args.step == "auto" and not fp8))
     if fused:
         last = case.context_lens.astype(np.int64) - 1
         table_slots = case.block_tables[np.arange(case.num_seqs), last // case.block_size].astype(np.int64) * \
@@ -264,26 +274,33 @@ def run_one(args, config):
         torch.cuda.synchronize()
         del src, dst
 
+    cur = [stream]  # the stream the step launches on (a capture stream while a graph records it)
+
     def write_only():
         if fp8:
             P.pa_cache_write_fp8(new_k, new_v, new_slots, k_cache, v_cache, k_scale, v_scale,
-                                 stream=stream)
+                                 stream=cur[0])
         else:
-            P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=stream)
+            P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=cur[0])
 
     def decode_only():
-        if fused:
+        if fused and fp8:
+            P.pa_decode_fp8_append(out, q, new_k, new_v, k_cache, v_cache, tables, ctx, case.scale,
+                                   k_scale, v_scale, case.block_size, case.num_kv_heads,
+                                   max_context_len=mcl, partition_size=partition, workspace=ws,
+                                   stream=cur[0])
+        elif fused:
             P.pa_decode_append(out, q, new_k, new_v, k_cache, v_cache, tables, ctx, case.scale,
                                case.block_size, case.num_kv_heads, max_context_len=mcl,
-                               partition_size=partition, workspace=ws, stream=stream)
+                               partition_size=partition, workspace=ws, stream=cur[0])
         elif fp8:
             P.pa_decode_fp8(out, q, k_cache, v_cache, tables, ctx, case.scale, k_scale, v_scale,
                             case.block_size, case.num_kv_heads, max_context_len=mcl,
-                            partition_size=partition, workspace=ws, stream=stream)
+                            partition_size=partition, workspace=ws, stream=cur[0])
         else:
             P.pa_decode(out, q, k_cache, v_cache, tables, ctx, case.scale, case.block_size,
                         case.num_kv_heads, max_context_len=mcl, partition_size=partition,
-                        workspace=ws, stream=stream)
+                        workspace=ws, stream=cur[0])
 
     def step():
         if not fused:
@@ -291,7 +308,13 @@ def run_one(args, config):
         decode_only()
 
     def stream_kernel():  # the first of the step's two attention launches, on its own
-        if fused:
+        if fused and fp8:
+            P.pa_decode_fp8_append_partitions(out, q, new_k, new_v, k_cache, v_cache, tables, ctx,
+                                              case.scale, k_scale, v_scale, case.block_size,
+                                              case.num_kv_heads, max_context_len=mcl,
+                                              partition_size=partition, workspace=ws,
+                                              stream=stream)
+        elif fused:
             P.pa_decode_append_partitions(out, q, new_k, new_v, k_cache, v_cache, tables, ctx,
                                           case.scale, case.block_size, case.num_kv_heads,
                                           max_context_len=mcl, partition_size=partition,
@@ -311,12 +334,29 @@ def run_one(args, config):
         step()
     torch.cuda.synchronize()
 
+    # a serving loop replays one captured step per iteration: the host's launch work (Python
+    # marshalling, argument checks, two or three kernel launches) leaves the step
+    graph = None
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cur[0] = torch.cuda.current_stream(dev)
+            step()
+        cur[0] = stream
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+
     # the timed steps: nothing but the path's own launches between the two synchronisations
     # (an event recorded between two kernels costs several microseconds of GPU time)
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps" + (" (graph replays)" if graph is not None else ""))
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -394,13 +434,14 @@ def run_one(args, config):
                             f"sum {int(case.context_lens.sum())}",
             "partition_size": partition, "kv_bytes_per_step": kv_bytes,
             "kv_cache": "e4m3" if fp8 else ("f16" if case.dtype == np.float16 else "f32"),
-            "step": "pa_decode_append" if fused else
-                    ("pa_cache_write_fp8 + pa_decode_fp8" if fp8 else "pa_cache_write + pa_decode"),
+            "step": ("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else
+                    "pa_cache_write + pa_decode",
+            "graph": graph is not None,  # timed steps are replays of one captured HIP graph
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "pa_decode": {
-            "call": "pa_decode_append" if fused else ("pa_decode_fp8" if fp8 else "pa_decode"),
+            "call": ("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else "pa_decode",
             "us": round(per_call_ms["decode"] * 1e3, 2),
             "kv_gbs": round(kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
             "pct_hbm_peak": round(100.0 * kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),

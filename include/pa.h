@@ -254,6 +254,33 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_fp8_append -- pa_decode_append over E4M3 pools: k_new[s], v_new[s] (fp16) are
+ * stored as codes at position context_lens[s] - 1 (rounded as pa_cache_write_fp8 rounds,
+ * with k_scale / v_scale) and out is attention over the dequantized context, the new token
+ * included.  Equal bit for bit to pa_cache_write_fp8 (at the table's slot) followed by
+ * pa_decode_fp8; arguments, checks and stores otherwise as pa_decode_append and
+ * pa_decode_fp8.  pa_decode_fp8_append_partitions is its first launch alone (stores
+ * nothing); pa_decode_reduce with dtype PA_F16 merges its pieces.
+ */
+int pa_decode_fp8_append(void* out, const void* q, const void* k_new, const void* v_new,
+                         void* k_cache, void* v_cache, const int32_t* block_tables,
+                         const int32_t* context_lens, float scale, float k_scale, float v_scale,
+                         int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                         int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int64_t num_blocks, int32_t partition_size,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+int pa_decode_fp8_append_partitions(void* out, const void* q, const void* k_new, const void* v_new,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* block_tables, const int32_t* context_lens,
+                                    float scale, float k_scale, float v_scale, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                                    int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, int64_t num_blocks,
+                                    int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
  * pa_prefill -- causal attention of several query tokens per sequence (a prompt chunk)
  * over the paged cache: the prompt phase of [SOSP] section 2.1, taken in chunks as in
  * [SOSP] section 5.1 (item 5); [VATT] "3 分钟速读" point 1 measures such paged prefill
@@ -399,7 +426,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 5)
+#define PA_ABI_VERSION ((2 << 16) | 6)
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ from ._lib import (  # noqa: F401
     pa_decode_append,
     pa_decode_append_partitions,
     pa_decode_fp8,
+    pa_decode_fp8_append,
+    pa_decode_fp8_append_partitions,
     pa_decode_fp8_partitions,
     pa_decode_partitions,
     pa_decode_reduce,

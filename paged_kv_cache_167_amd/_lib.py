@@ -51,6 +51,15 @@ SIGNATURES = {
                                                _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                                _c_int32, _c_int32, _c_int64, _c_int32, _vp,
                                                ctypes.c_size_t, _vp]),
+    "pa_decode_fp8_append": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float,
+                                        ctypes.c_float, ctypes.c_float, _c_int32, _c_int32, _c_int32,
+                                        _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_int32,
+                                        _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_fp8_append_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                   ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                                   _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                                   _c_int32, _c_int32, _c_int64, _c_int32, _vp,
+                                                   ctypes.c_size_t, _vp]),
     "pa_cache_write_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
                                       _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _vp]),
     "pa_decode_fp8": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, ctypes.c_float,
@@ -313,6 +322,46 @@ def pa_decode_fp8_partitions(out, q, k_cache, v_cache, block_tables, context_len
                                        k_scale, v_scale, block_size, num_kv_heads, max_context_len,
                                        partition_size, workspace, stream)
     _check("pa_decode_fp8_partitions", lib().pa_decode_fp8_partitions(*args))
+    return workspace
+
+
+def _decode_fp8_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                            k_scale, v_scale, block_size, num_kv_heads, max_context_len,
+                            partition_size, workspace, stream):
+    import torch
+    if k_new.dtype != torch.float16 or v_new.dtype != torch.float16:
+        raise PaError("binding", PA_ERR_UNSUPPORTED, "k_new and v_new must be float16")
+    if k_new.shape != (q.shape[0], k_cache.shape[1], q.shape[2]) or v_new.shape != k_new.shape:
+        raise PaError("binding", PA_ERR_INVALID_ARG, "k_new and v_new must be [num_seqs, num_kv_heads, head_dim]")
+    args, workspace = _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                       k_scale, v_scale, block_size, num_kv_heads, max_context_len,
+                                       partition_size, workspace, stream)
+    return args[:2] + (_ptr(k_new), _ptr(v_new)) + args[2:], workspace
+
+
+def pa_decode_fp8_append(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens, scale,
+                         k_scale, v_scale, block_size, num_kv_heads, max_context_len=None,
+                         partition_size=DEFAULT_PARTITION, workspace=None, stream=None):
+    """pa_decode_append over E4M3 pools: store the new tokens' codes, attend over the codes
+    times k_scale / v_scale."""
+    args, workspace = _decode_fp8_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                              context_lens, scale, k_scale, v_scale, block_size,
+                                              num_kv_heads, max_context_len, partition_size, workspace,
+                                              stream)
+    _check("pa_decode_fp8_append", lib().pa_decode_fp8_append(*args))
+    return workspace
+
+
+def pa_decode_fp8_append_partitions(out, q, k_new, v_new, k_cache, v_cache, block_tables, context_lens,
+                                    scale, k_scale, v_scale, block_size, num_kv_heads,
+                                    max_context_len=None, partition_size=DEFAULT_PARTITION,
+                                    workspace=None, stream=None):
+    """First launch of pa_decode_fp8_append alone (stores nothing)."""
+    args, workspace = _decode_fp8_append_args(out, q, k_new, v_new, k_cache, v_cache, block_tables,
+                                              context_lens, scale, k_scale, v_scale, block_size,
+                                              num_kv_heads, max_context_len, partition_size, workspace,
+                                              stream)
+    _check("pa_decode_fp8_append_partitions", lib().pa_decode_fp8_append_partitions(*args))
     return workspace
 
 

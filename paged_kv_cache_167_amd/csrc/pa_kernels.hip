@@ -419,19 +419,22 @@ struct StreamArgs {
   // ([num_seqs, num_kv_heads, head_dim]) instead of the pools
   const char* k_new;
   const char* v_new;
+  float k_inv, v_inv;  // E4M3 append mode: the reciprocal scales the new rows are coded with
 };
 
 // Append mode of the reduce kernel: where the new tokens' rows go (k_new == nullptr: off).
 struct AppendArgs {
-  const u32x4* k_new;  // [num_seqs, num_kv_heads, head_dim] rows, in 16-byte chunks
-  const u32x4* v_new;
-  u32x4* k_cache;  // the pools
-  u32x4* v_cache;
+  const char* k_new;  // [num_seqs, num_kv_heads, head_dim] rows of the pools' element type, or
+  const char* v_new;  // fp16 rows for E4M3 pools
+  char* k_cache;      // the pools
+  char* v_cache;
   const int32_t* block_tables;
   int max_blocks_per_seq;
   int block_size;
   int num_kv_heads;
   int64_t num_blocks;
+  int codes;           // E4M3 pools: store code(x * inv) of each element
+  float k_inv, v_inv;  // 1/k_scale and 1/v_scale rounded to fp32
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -1203,6 +1206,64 @@ __device__ __forceinline__ void load_entries4(const int32_t* a0, const int32_t* 
       : "memory");
 }
 
+// The value of the E4M3 code of y (e4m3_code), computed without the code and without
+// branches: round to nearest even at 3 mantissa bits in the normal range, to a multiple of
+// 2^-9 below 2^-6, 448 from 448 up, NaN for NaN.  Values of codes are exact in fp16.
+__device__ __forceinline__ float e4m3_value_of(float y) {
+  const uint32_t bits = as_u(y);
+  const uint32_t mag = bits & 0x7FFFFFFFu;
+  const float a = as_f(mag);
+  const float normal = as_f((mag + 0x7FFFFu + ((mag >> 20) & 1u)) & 0xFFF00000u);
+  const float sub = __builtin_rintf(a * 512.0f) * (1.0f / 512.0f);
+  float q = a >= 0.015625f ? normal : sub;
+  q = a >= 448.0f ? 448.0f : q;
+  return as_f(as_u(q) | (bits & 0x80000000u));
+}
+
+// Eight fp16 values times inv, each replaced by the fp16 value of its E4M3 code.
+__device__ __forceinline__ f16x8 e4m3_values8(const u32x4& x, float inv) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const f16x2 h = word_as<f16x2>(x, i / 2);
+    r[i] = static_cast<f16>(e4m3_value_of(static_cast<float>(h[i % 2]) * inv));
+  }
+  return r;
+}
+
+// E4M3 append mode: read the new token's fp16 rows from a stage's new-row area (K row at
+// OFF, V row at OFF + 2 D): k[kb] = the 8 K values of dims 8 (jq KB + kb) .. + 7 (at the
+// lane's address nk + 16 kb), v = the NB V values of dims NB g .. NB g + NB - 1 (at nv;
+// D = 64 fills the low half).  asm for the same reason as the stage reads.
+template <int D, int OFF>
+__device__ __forceinline__ void read_new_rows_f8(uint32_t nk, uint32_t nv, u32x4 (&k)[D / 32], u32x4& v) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %[k0], %[a] offset:%[o0]\n\t"
+        "ds_read_b128 %[k1], %[a] offset:%[o1]\n\t"
+        "ds_read_b128 %[k2], %[a] offset:%[o2]\n\t"
+        "ds_read_b128 %[k3], %[a] offset:%[o3]\n\t"
+        "ds_read_b128 %[v0], %[b] offset:%[ov]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [k2] "=&v"(k[2]), [k3] "=&v"(k[3]), [v0] "=&v"(v)
+        : [a] "v"(nk), [b] "v"(nv), [o0] "n"(OFF), [o1] "n"(OFF + 16), [o2] "n"(OFF + 32),
+          [o3] "n"(OFF + 48), [ov] "n"(OFF + 2 * D)
+        : "memory");
+  } else {
+    static_assert(D == 64, "head_dim");
+    u32x2 h;
+    asm volatile(
+        "ds_read_b128 %[k0], %[a] offset:%[o0]\n\t"
+        "ds_read_b128 %[k1], %[a] offset:%[o1]\n\t"
+        "ds_read_b64 %[v0], %[b] offset:%[ov]\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : [k0] "=&v"(k[0]), [k1] "=&v"(k[1]), [v0] "=&v"(h)
+        : [a] "v"(nk), [b] "v"(nv), [o0] "n"(OFF), [o1] "n"(OFF + 16), [ov] "n"(OFF + 2 * D)
+        : "memory");
+    v = u32x4{h[0], h[1], 0u, 0u};
+  }
+}
+
 // Read a piece's q operand from LDS: chunks kb = 0 .. KB-1 at the lane's address + OFF +
 // 16 kb.  Called after the stage wait that covers the q loads; asm for the same reason
 // as the stage reads.
@@ -1242,16 +1303,22 @@ __device__ __forceinline__ void unroll(F&& f) {
 }
 
 // F8: E4M3 pools.  DENSE: the virtually contiguous cache of pa_decode_dense (fp16, no table).
-// APPEND: each sequence's newest token (position ctx - 1) comes from a.k_new / a.v_new, not
-// from the pools, which the same call writes only after this kernel (pa_decode_append).
+// APPEND: each sequence's newest token (position ctx - 1) comes from a.k_new / a.v_new (fp16
+// rows), not from the pools, which the same call writes only after this kernel
+// (pa_decode_append, pa_decode_fp8_append).  fp16 pools load that row in place of the
+// pool's; E4M3 pools stage the fp16 rows beside the tile and replace the token's operands
+// with the values of their codes.
 template <int D, int NST, bool F8, bool DENSE = false, bool APPEND = false>
 __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs a) {
   static_assert(!(F8 && DENSE), "the contiguous cache is fp16");
-  static_assert(!APPEND || (!F8 && !DENSE), "append mode reads fp16 pools");
+  static_assert(!(APPEND && DENSE), "append mode reads the pools");
   using K = MCfg<D, F8>;
   constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
   constexpr int ROWQ = K::kRowQ, NCQ = K::kNCQ;
-  constexpr int LOADS = K::kLoads, STAGE = K::kStage, HALF = K::kHalf;
+  constexpr int LOADS = K::kLoads, HALF = K::kHalf;
+  constexpr bool F8NEW = APPEND && F8;  // E4M3 append: the new fp16 rows get a stage area
+  constexpr int NEWOFF = K::kStage;     // K row (2 D bytes), then V row
+  constexpr int STAGE = F8NEW ? (K::kStage + 4 * D + 1023) / 1024 * 1024 : K::kStage;
   constexpr int QOFF = 2 * HALF;             // q rows within a stage
   constexpr int QROWS = 1024 / ROWQ;         // q rows per 1 KB load
   constexpr int KR = D / 64;                 // E4M3: 16-byte K reads per lane
@@ -1407,7 +1474,19 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
                         static_cast<uint64_t>(tok0 & (bsz - 1)) * ROW;
     const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
-    if constexpr (APPEND) {
+    if constexpr (F8NEW) {
+      // the context's last tile: its new K and V rows (fp16, 16-byte chunks) go to the stage's
+      // new-row area, one chunk per lane, ahead of the tile's loads so that the same stage
+      // wait covers them
+      constexpr int NCN = 2 * D / 16;
+      if (real && tok0 + TK >= f.ctx && lane < 2 * NCN) {
+        const int64_t nrow = (static_cast<int64_t>(f.s) * a.num_kv_heads + kvh) * (2 * D);
+        const char* src = (lane < NCN ? a.k_new : a.v_new) + nrow + (lane % NCN) * 16;
+        __builtin_amdgcn_global_load_lds(static_cast<const void*>(src), static_cast<void*>(stage + NEWOFF), 16, 0,
+                                         0);
+      }
+    }
+    if constexpr (APPEND && !F8) {
       if (real && tok0 + TK >= f.ctx) {  // the context's last tile: row ctx - 1 - tok0 is new
         const int rn = f.ctx - 1 - tok0;
         const int64_t nrow = (static_cast<int64_t>(f.s) * a.num_kv_heads + kvh) * ROW;
@@ -1581,10 +1660,42 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   f16x8 kop[KB];
   f16x4 vop[NB];
   bool fbad[NST];
+  // E4M3 append mode: this lane's addresses in a stage's new-row area
+  const uint32_t nk_addr = ring + static_cast<uint32_t>(16 * jq * KB);
+  const uint32_t nv_addr = ring + static_cast<uint32_t>(2 * NB * g);
   auto process = [&](int i, auto stc) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
     if (i == 0 || cc.t == 0) piece_start(stc);
     piece_bad |= fbad[st];
+    if constexpr (F8NEW) {
+      if (cc.t == cc.nt - 1) {  // the segment's last tile holds the new token, row rn
+        // the operands of row rn become the values of the codes the reduce kernel stores
+        // for it: code(x * 1/scale), expanded exactly, as for every other row
+        const int tn = tau(cc.ctx - 1 - cc.t * TK);  // its product row (tau is an involution)
+        u32x4 nkr[KB], nvr;
+        read_new_rows_f8<D, st * STAGE + NEWOFF>(nk_addr, nv_addr, nkr, nvr);
+        if (g == tn) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            kop[kb] = e4m3_values8(nkr[kb], a.k_inv);
+          }
+        }
+        if (jq == (tn >> 2)) {
+          const int t = tn & 3;
+          const f16x8 qv = e4m3_values8(nvr, a.v_inv);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const f16 val = qv[nb];
+            f16x4 x = vop[nb];
+            x[0] = t == 0 ? val : x[0];
+            x[1] = t == 1 ? val : x[1];
+            x[2] = t == 2 ? val : x[2];
+            x[3] = t == 3 ? val : x[3];
+            vop[nb] = x;
+          }
+        }
+      }
+    }
     consume(min(TK, cc.ctx - cc.t * TK), kop, vop);
     if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
     wk.advance(cc);
@@ -2116,17 +2227,32 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
   if (ap.k_new != nullptr && h == kvh * group && ctx >= 1 && ctx <= max_context_len) {
     // append mode: the first query head of each kv head stores the new token's K and V
     // rows at position ctx - 1 (the stream kernel read them from k_new / v_new)
-    constexpr int kChunks = D * static_cast<int>(sizeof(T)) / 16;  // 16-byte chunks per row
-    static_assert(2 * kChunks <= kWave, "one lane per chunk of the K and V rows");
+    constexpr int kIn = D * static_cast<int>(sizeof(T));  // bytes of an input row
+    static_assert(2 * (kIn / 16) <= kWave, "one lane per 16 bytes of the K and V rows");
     const int64_t blk = ap.block_tables[static_cast<int64_t>(s) * ap.max_blocks_per_seq +
                                         (ctx - 1) / ap.block_size];
-    if (blk >= 0 && blk < ap.num_blocks && lane < 2 * kChunks) {
-      const int c = lane % kChunks;
-      const int64_t row = (static_cast<int64_t>(s) * ap.num_kv_heads + kvh) * kChunks + c;
-      const int64_t slot = ((blk * ap.num_kv_heads + kvh) * ap.block_size + (ctx - 1) % ap.block_size) *
-                               kChunks + c;
-      if (lane < kChunks) ap.k_cache[slot] = ap.k_new[row];
-      else ap.v_cache[slot] = ap.v_new[row];
+    const int64_t row = static_cast<int64_t>(s) * ap.num_kv_heads + kvh;
+    const int64_t slot = (blk * ap.num_kv_heads + kvh) * ap.block_size + (ctx - 1) % ap.block_size;
+    if (blk >= 0 && blk < ap.num_blocks) {
+      if (ap.codes) {  // one lane per 16 codes: two 16-byte chunks of fp16 in, one out
+        constexpr int kC = D / 16;
+        if (lane < 2 * kC) {
+          const int c = lane % kC;
+          const bool isv = lane >= kC;
+          const char* src = (isv ? ap.v_new : ap.k_new) + row * (2 * D) + c * 32;
+          const float inv = isv ? ap.v_inv : ap.k_inv;
+          const u32x2 lo = encode8(*reinterpret_cast<const u32x4*>(src), inv);
+          const u32x2 hi = encode8(*reinterpret_cast<const u32x4*>(src + 16), inv);
+          *reinterpret_cast<u32x4*>((isv ? ap.v_cache : ap.k_cache) + slot * D + c * 16) =
+              u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+      } else if (lane < 2 * (kIn / 16)) {  // one lane per 16-byte chunk
+        constexpr int kC = kIn / 16;
+        const int c = lane % kC;
+        const bool isv = lane >= kC;
+        *reinterpret_cast<u32x4*>((isv ? ap.v_cache : ap.k_cache) + slot * kIn + c * 16) =
+            *reinterpret_cast<const u32x4*>((isv ? ap.v_new : ap.k_new) + row * kIn + c * 16);
+      }
     }
   }
   if (ctx <= 0 || ctx > max_context_len) {  // nothing to attend over: zeros; invalid: NaN
@@ -2152,6 +2278,9 @@ using pa_detail::fail;
 using pa_detail::g_error;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// E4M3 stores multiply by the reciprocal scale, rounded once to fp32
+float inv_scale(float scale) { return static_cast<float>(1.0 / static_cast<double>(scale)); }
 
 int log2_of(int x) {
   int l = 0;
@@ -2314,10 +2443,15 @@ struct Residency {
   int waves = 0, cus = 0;
 };
 
+// Resident waves of a one-wave kernel on the current device, memoised per (device, kernel).
+// A full table only stops the memoising: the answer is the same either way, since the work
+// split, and with it the rounding of every split context, depends on it.  {0, 0} if the
+// runtime cannot say.
 Residency residency(const void* kernel) {
+  constexpr int kSlots = 32;
   static std::mutex mu;
-  static const void* keys[64][8] = {};
-  static Residency vals[64][8];
+  static const void* keys[64][kSlots] = {};
+  static Residency vals[64][kSlots];
   int dev = 0;
   Residency r;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -2325,22 +2459,26 @@ Residency residency(const void* kernel) {
     return r;
   }
   std::lock_guard<std::mutex> lock(mu);
-  for (int i = 0; i < 8; ++i) {
+  int slot = -1;
+  for (int i = 0; i < kSlots; ++i) {
     if (keys[dev][i] == kernel) return vals[dev][i];
     if (keys[dev][i] == nullptr) {
-      int per_cu = 0, cus = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess ||
-          hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-          per_cu <= 0 || cus <= 0) {
-        (void)hipGetLastError();
-        return r;
-      }
-      r.waves = per_cu * cus;
-      r.cus = cus;
-      keys[dev][i] = kernel;
-      vals[dev][i] = r;
-      return r;
+      slot = i;
+      break;
     }
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || per_cu <= 0 ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    return r;
+  }
+  r.waves = per_cu * cus;
+  r.cus = cus;
+  if (slot >= 0) {
+    keys[dev][slot] = kernel;
+    vals[dev][slot] = r;
   }
   return r;
 }
@@ -2358,15 +2496,19 @@ int waves_for(const DecodeCall& c, const Geom& g, int64_t base) {
 // fp32: every resident wave (at most kMaxWaves).  fp16: kMfWavesPerCU per compute unit:
 // a few deep streams per unit keep HBM busy with less contention than a full unit.
 // E4M3 pools: kF8WavesPerCU shallower streams.
+// Both return 0 when the residency query fails (the launch then reports an error rather than
+// pick another split).
 template <typename T, int D, int GT>
 int waves_valu(const DecodeCall& c, const Geom& g) {
   const Residency r = residency(reinterpret_cast<const void*>(pa_stream_kernel<T, D, GT>));
+  if (r.waves <= 0) return 0;
   return waves_for(c, g, r.waves > kMaxWaves ? kMaxWaves : r.waves);
 }
 
 template <int D, int NST, bool F8, bool DENSE, bool APPEND>
 int waves_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   const Residency r = residency(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>));
+  if (r.waves <= 0) return 0;
   int64_t base = static_cast<int64_t>(r.cus) * waves_per_cu;
   if (base > r.waves) base = r.waves;
   return waves_for(c, g, base);
@@ -2414,6 +2556,8 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   }
   a.k_new = static_cast<const char*>(c.k_new);
   a.v_new = static_cast<const char*>(c.v_new);
+  a.k_inv = inv_scale(c.k_scale);
+  a.v_inv = inv_scale(c.v_scale);
   return a;
 }
 
@@ -2421,6 +2565,7 @@ template <typename T, int D, int GT>
 int launch_stream(const DecodeCall& c, const Geom& g) {
   StreamArgs a = stream_args(c, g);
   a.num_waves = waves_valu<T, D, GT>(c, g);
+  if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_kernel failed");
   hipLaunchKernelGGL((pa_stream_kernel<T, D, GT>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_kernel launch");
 }
@@ -2430,6 +2575,7 @@ template <int D, int NST, bool F8, bool DENSE = false, bool APPEND = false>
 int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
   a.num_waves = waves_mfma<D, NST, F8, DENSE, APPEND>(c, g, waves_per_cu);
+  if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_mfma_kernel failed");
   hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>), dim3(a.num_waves), dim3(kWave), 0, c.stream,
                      a);
   return check_hip("pa_stream_mfma_kernel launch");
@@ -2440,15 +2586,18 @@ int launch_reduce(const DecodeCall& c, const Geom& g) {
   const WsParts ws = split_workspace(c.workspace, g);
   AppendArgs ap{};  // k_new == nullptr: the reduce writes no cache row
   if (c.k_new) {
-    ap.k_new = static_cast<const u32x4*>(c.k_new);
-    ap.v_new = static_cast<const u32x4*>(c.v_new);
-    ap.k_cache = static_cast<u32x4*>(const_cast<void*>(c.k_cache));
-    ap.v_cache = static_cast<u32x4*>(const_cast<void*>(c.v_cache));
+    ap.k_new = static_cast<const char*>(c.k_new);
+    ap.v_new = static_cast<const char*>(c.v_new);
+    ap.k_cache = static_cast<char*>(const_cast<void*>(c.k_cache));
+    ap.v_cache = static_cast<char*>(const_cast<void*>(c.v_cache));
     ap.block_tables = c.block_tables;
     ap.max_blocks_per_seq = c.max_blocks_per_seq;
     ap.block_size = c.block_size;
     ap.num_kv_heads = c.num_kv_heads;
     ap.num_blocks = c.num_blocks;
+    ap.codes = c.kv_fp8 ? 1 : 0;
+    ap.k_inv = inv_scale(c.k_scale);
+    ap.v_inv = inv_scale(c.v_scale);
   }
   hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
                      c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
@@ -2471,7 +2620,9 @@ template <int Which, int D>
 int dispatch_f16(const DecodeCall& c, const Geom& g) {
   if (Which == 1) return launch_reduce<f16, D, kMfRows>(c, g);
   if (c.dense) return launch_stream_mfma<D, kMfStages, false, true>(c, g, kMfWavesPerCU);
-  if (c.k_new) return launch_stream_mfma<D, kMfStages, false, false, true>(c, g, kMfWavesPerCU);
+  if (c.k_new)
+    return c.kv_fp8 ? launch_stream_mfma<D, kF8Stages, true, false, true>(c, g, kF8WavesPerCU)
+                    : launch_stream_mfma<D, kMfStages, false, false, true>(c, g, kMfWavesPerCU);
   return c.kv_fp8 ? launch_stream_mfma<D, kF8Stages, true>(c, g, kF8WavesPerCU)
                   : launch_stream_mfma<D, kMfStages, false>(c, g, kMfWavesPerCU);
 }
@@ -2745,8 +2896,8 @@ int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping
     return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
   // the reciprocal is rounded once, to fp32; every element is then one fp32 product
-  const float k_inv = static_cast<float>(1.0 / static_cast<double>(k_scale));
-  const float v_inv = static_cast<float>(1.0 / static_cast<double>(v_scale));
+  const float k_inv = inv_scale(k_scale);
+  const float v_inv = inv_scale(v_scale);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return head_dim == 64
              ? launch_cache_write_fp8<64>(k, v, slot_mapping, k_cache, v_cache, k_inv, v_inv, num_tokens,
@@ -2755,12 +2906,13 @@ int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping
                                            num_kv_heads, block_size, num_blocks, st);
 }
 
-static int decode_fp8(int launches, void* out, const void* q, const void* k_cache, const void* v_cache,
-                      const int32_t* block_tables, const int32_t* context_lens, float scale, float k_scale,
-                      float v_scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
-                      int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
-                      int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+// k_new == nullptr: pa_decode_fp8; otherwise the append form (new fp16 rows in k_new / v_new)
+static int decode_fp8(int launches, const void* k_new, const void* v_new, void* out, const void* q,
+                      const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, float k_scale, float v_scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
   g_error.clear();
   DecodeCall c = make_call(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                            num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
@@ -2769,6 +2921,8 @@ static int decode_fp8(int launches, void* out, const void* q, const void* k_cach
   c.kv_fp8 = true;
   c.k_scale = k_scale;
   c.v_scale = v_scale;
+  c.k_new = k_new;
+  c.v_new = v_new;
   if (!valid_scale(k_scale) || !valid_scale(v_scale))
     return fail(PA_ERR_INVALID_ARG, "k_scale %g and v_scale %g must be positive and finite",
                 static_cast<double>(k_scale), static_cast<double>(v_scale));
@@ -2788,7 +2942,8 @@ int pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_c
                   int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
                   int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  return decode_fp8(2, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+  return decode_fp8(2, nullptr, nullptr, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                    v_scale,
                     block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                     max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
 }
@@ -2799,8 +2954,40 @@ int pa_decode_fp8_partitions(void* out, const void* q, const void* k_cache, cons
                              int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
                              int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
                              int32_t partition_size, void* workspace, size_t workspace_bytes, void* stream) {
-  return decode_fp8(1, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale, v_scale,
+  return decode_fp8(1, nullptr, nullptr, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                    v_scale,
                     block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                    max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_fp8_append(void* out, const void* q, const void* k_new, const void* v_new, void* k_cache,
+                         void* v_cache, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                         float k_scale, float v_scale, int32_t block_size, int32_t num_kv_heads,
+                         int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                         int32_t max_context_len, int64_t num_blocks, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) {
+    g_error.clear();
+    return fail(PA_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  }
+  return decode_fp8(2, k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                    v_scale, block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                    max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_fp8_append_partitions(void* out, const void* q, const void* k_new, const void* v_new,
+                                    const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                    const int32_t* context_lens, float scale, float k_scale, float v_scale,
+                                    int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                                    int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                    int32_t max_context_len, int64_t num_blocks, int32_t partition_size,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!k_new || !v_new)) {
+    g_error.clear();
+    return fail(PA_ERR_INVALID_ARG, "k_new or v_new is NULL");
+  }
+  return decode_fp8(1, k_new, v_new, out, q, k_cache, v_cache, block_tables, context_lens, scale, k_scale,
+                    v_scale, block_size, num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
                     max_context_len, num_blocks, partition_size, workspace, workspace_bytes, stream);
 }
 

@@ -27,7 +27,8 @@ def test_header_declares_the_calls():
     for want in ("pa_cache_write", "pa_decode", "pa_decode_workspace_bytes",
                  "pa_decode_partitions", "pa_decode_reduce", "pa_last_error", "pa_abi_version",
                  "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_fp8_partitions",
-                 "pa_prefill", "pa_decode_append", "pa_decode_append_partitions"):
+                 "pa_prefill", "pa_decode_append", "pa_decode_append_partitions",
+                 "pa_decode_fp8_append", "pa_decode_fp8_append_partitions"):
         assert want in names
 
 
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 5
+    assert P.lib().pa_abi_version() == (2 << 16) | 6
 
 
 def test_workspace_size_query():
@@ -183,6 +184,35 @@ def test_decode_append_binding_takes_fp16_only():
     pool = torch.zeros((3, 2, 16, 64), dtype=torch.float32)
     with pytest.raises(P.PaError):
         P.pa_decode_append(h, h, h[:, :2], h[:, :2], pool, pool, None, None, 0.1, 16, 2)
+
+
+def _append_fp8(fn="pa_decode_fp8_append", **over):
+    a = dict(out=FAKE, q=FAKE, kn=FAKE, vn=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, scale=0.1, ks=0.01,
+             vs=0.02, B=16, hkv=8, S=4, hq=32, D=128, mb=16, mcl=256, N=100, P=64, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(over)
+    return getattr(P.lib(), fn)(a["out"], a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["bt"], a["ctx"],
+                                a["scale"], a["ks"], a["vs"], a["B"], a["hkv"], a["S"], a["hq"], a["D"],
+                                a["mb"], a["mcl"], a["N"], a["P"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_fp8_append", "pa_decode_fp8_append_partitions"])
+@pytest.mark.parametrize("over,code", [
+    (dict(kn=None), _lib.PA_ERR_INVALID_ARG),
+    (dict(vn=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
+    (dict(ks=0.0), _lib.PA_ERR_INVALID_ARG),
+    (dict(vs=float("inf")), _lib.PA_ERR_INVALID_ARG),
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(hq=30), _lib.PA_ERR_INVALID_ARG),
+    (dict(wsb=16), _lib.PA_ERR_WORKSPACE),
+])
+def test_decode_fp8_append_rejects_bad_arguments(fn, over, code):
+    assert _append_fp8(fn, **over) == code
+    assert P.last_error() != ""
+
+
+def test_decode_fp8_append_with_no_sequences_is_a_no_op():
+    assert _append_fp8(S=0, out=None, q=None, kn=None, vn=None) == _lib.PA_OK
 
 
 def _decode_fp8(fn="pa_decode_fp8", **over):

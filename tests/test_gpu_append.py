@@ -150,3 +150,124 @@ def test_empty_invalid_and_out_of_pool_sequences_store_nothing():
     assert _same_bits(kc, ek) and _same_bits(vc, ev)
     ref, _, _ = _two_calls(case, d, 0)
     assert got[[0, 4]].tobytes() == ref[[0, 4]].tobytes()
+
+
+# ------------------------------------------------------------------ E4M3 pools
+def _f8():
+    from tests import test_gpu_fp8 as F
+    return F
+
+
+def _f8_device(case, ks, vs):
+    """Pools of codes holding every token but the new ones; the new rows as fp16."""
+    torch = _torch()
+    F = _f8()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    d = type("D", (), {})()
+    d.q, d.tables, d.ctx = t(case.q), t(case.block_tables), t(case.context_lens)
+    d.k_cache, d.v_cache = t(F._empty_codes(case)), t(F._empty_codes(case))
+    P.pa_cache_write_fp8(t(case.prefix_k), t(case.prefix_v), t(case.prefix_slots), d.k_cache, d.v_cache,
+                         ks, vs)
+    d.new_k, d.new_v, d.new_slots = t(case.new_k), t(case.new_v), t(case.new_slots)
+    torch.cuda.synchronize()
+    return d
+
+
+def _f8_two_calls(case, d, ks, vs, partition):
+    torch = _torch()
+    kc, vc = d.k_cache.clone(), d.v_cache.clone()
+    P.pa_cache_write_fp8(d.new_k, d.new_v, d.new_slots, kc, vc, ks, vs)
+    out = torch.empty_like(d.q)
+    P.pa_decode_fp8(out, d.q, kc, vc, d.tables, d.ctx, case.scale, ks, vs, case.block_size,
+                    case.num_kv_heads, max_context_len=case.max_context_len, partition_size=partition)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), kc, vc
+
+
+def _f8_append(case, d, ks, vs, partition, ctx=None, tables=None):
+    torch = _torch()
+    kc, vc = d.k_cache.clone(), d.v_cache.clone()
+    out = torch.empty_like(d.q)
+    P.pa_decode_fp8_append(out, d.q, d.new_k, d.new_v, kc, vc, d.tables if tables is None else tables,
+                           d.ctx if ctx is None else ctx, case.scale, ks, vs, case.block_size,
+                           case.num_kv_heads, max_context_len=case.max_context_len,
+                           partition_size=partition)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), kc, vc
+
+
+F8_SHAPES = [(128, 16, 32, 8), (128, 8, 16, 2), (128, 32, 14, 2), (64, 16, 8, 8), (64, 8, 12, 2),
+             (128, 16, 64, 2)]
+
+
+@pytest.mark.parametrize("partition", [0, 64])
+@pytest.mark.parametrize("D,B,hq,hkv", F8_SHAPES)
+def test_fp8_equals_write_then_decode_and_the_oracle(D, B, hq, hkv, partition):
+    F = _f8()
+    label = f"fp8 append D{D} B{B} {hq}/{hkv} P{partition}"
+    G.say(label)
+    case = W.make_case(seed=3 * D + B + hq + partition, dtype=np.float16, context_lens=CTX,
+                       num_q_heads=hq, num_kv_heads=hkv, head_dim=D, block_size=B, sigma=0.5)
+    assert np.array_equal(_table_slots(case), case.new_slots)
+    ks, vs = F._scales(case)
+    d = _f8_device(case, ks, vs)
+    got, kc, vc = _f8_append(case, d, ks, vs, partition)
+    ref, rkc, rvc = _f8_two_calls(case, d, ks, vs, partition)
+    assert got.tobytes() == ref.tobytes(), f"{label}: output differs from write + decode"
+    assert bool(torch_equal(kc, rkc)) and bool(torch_equal(vc, rvc)), f"{label}: pools differ"
+    okc, ovc = F._oracle_pools(case, ks, vs)
+    assert kc.cpu().numpy().tobytes() == okc.tobytes(), f"{label}: K codes differ from the oracle's"
+    assert vc.cpu().numpy().tobytes() == ovc.tobytes(), f"{label}: V codes differ from the oracle's"
+    F._check(got, F._oracle_decode(case, okc, ovc, ks, vs), ovc, vs, label)
+
+
+def torch_equal(a, b):
+    return _torch().equal(a, b)  # uint8 codes: NaN codes compare as bytes
+
+
+@pytest.mark.parametrize("name", ["llama3_8b", "llama2_70b"])
+def test_fp8_workloads_equal_write_then_decode(name):
+    F = _f8()
+    G.say(f"fp8 append {name}")
+    case = W.CONFIGS[name]("plain")
+    ks, vs = F._scales(case)
+    d = _f8_device(case, ks, vs)
+    got, kc, vc = _f8_append(case, d, ks, vs, 0)
+    ref, rkc, rvc = _f8_two_calls(case, d, ks, vs, 0)
+    assert got.tobytes() == ref.tobytes()
+    assert torch_equal(kc, rkc) and torch_equal(vc, rvc)
+
+
+def test_fp8_split_launches_and_nothing_stored_for_bad_sequences():
+    torch = _torch()
+    F = _f8()
+    case = W.make_case(seed=93, dtype=np.float16, context_lens=[40, 70, 33, 90, 17, 1, 16], num_q_heads=8,
+                       num_kv_heads=2, head_dim=128, block_size=16, sigma=0.5)
+    ks, vs = F._scales(case)
+    d = _f8_device(case, ks, vs)
+    one, _, _ = _f8_append(case, d, ks, vs, 64)
+    kc, vc = d.k_cache.clone(), d.v_cache.clone()
+    out = torch.empty_like(d.q)
+    ws = P.pa_decode_fp8_append_partitions(out, d.q, d.new_k, d.new_v, kc, vc, d.tables, d.ctx, case.scale,
+                                           ks, vs, case.block_size, case.num_kv_heads,
+                                           max_context_len=case.max_context_len, partition_size=64)
+    P.pa_decode_reduce(out, d.ctx, case.num_kv_heads, case.max_context_len, 64, ws)
+    torch.cuda.synchronize()
+    assert out.cpu().numpy().tobytes() == one.tobytes()
+    assert torch_equal(kc, d.k_cache) and torch_equal(vc, d.v_cache)  # the first launch stores nothing
+    ctx = d.ctx.clone()
+    ctx[1] = 0
+    ctx[2] = case.max_context_len + 5
+    tables = d.tables.clone()
+    tables[3, (int(case.context_lens[3]) - 1) // 16] = case.num_blocks + 3
+    got, kc, vc = _f8_append(case, d, ks, vs, 0, ctx=ctx, tables=tables)
+    assert np.all(got[1] == 0)
+    assert np.all(np.isnan(got[2])) and np.all(np.isnan(got[3]))
+    keep = torch.tensor([0, 4, 5, 6], device="cuda")
+    ek, ev = d.k_cache.clone(), d.v_cache.clone()
+    P.pa_cache_write_fp8(d.new_k[keep].contiguous(), d.new_v[keep].contiguous(), d.new_slots[keep].contiguous(),
+                         ek, ev, ks, vs)
+    torch.cuda.synchronize()
+    assert torch_equal(kc, ek) and torch_equal(vc, ev)
+    ref, _, _ = _f8_two_calls(case, d, ks, vs, 0)
+    assert got[[0, 4, 5, 6]].tobytes() == ref[[0, 4, 5, 6]].tobytes()

@@ -123,3 +123,40 @@ def test_contexts_of_zero_and_invalid_lengths():
     G.assert_close(got[[0, 2]], ref[[0, 2]], np.float16, "others")
     assert np.isfinite(full).all()
     kv.close()
+
+
+def test_dense_equals_paged_after_many_other_kernels():
+    """The work split depends on the resident-wave count of each kernel, which the library
+    memoises.  Regression: with more kernels in use than its table held, a kernel seen late got
+    another split (and different rounding) than the paged kernel seen early.  Here the paged
+    kernel runs first, then a dozen other decode kernels, then the dense one."""
+    torch = _torch()
+    case = W.make_case(seed=65, dtype=np.float16, context_lens=[1, 15, 16, 17, 1023, 1024, 1025, 2049, 3000],
+                       num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, sigma=0.5)
+    d = G.to_device(case)
+    paged = G.decode(case, d)
+    for D, hq, hkv in ((64, 4, 4), (64, 8, 4), (64, 16, 4), (64, 32, 4),
+                       (128, 4, 4), (128, 8, 4), (128, 16, 4), (128, 32, 4)):  # every fp32 group tile
+        other = W.make_case(seed=66, dtype=np.float32, context_lens=[5, 40], num_q_heads=hq, num_kv_heads=hkv,
+                            head_dim=D, block_size=16, sigma=0.5)
+        G.decode(other, G.to_device(other))
+    for D in (64, 128):  # fp16 at the other head size, E4M3 and append kernels
+        other = W.make_case(seed=67, dtype=np.float16, context_lens=[5, 40], num_q_heads=8, num_kv_heads=2,
+                            head_dim=D, block_size=16, sigma=0.5)
+        od = G.to_device(other, write_new=False)
+        out = torch.empty_like(od.q)
+        P.pa_decode_append(out, od.q, od.new_k, od.new_v, od.k_cache, od.v_cache, od.tables, od.ctx,
+                           other.scale, 16, 2, max_context_len=other.max_context_len)
+        codes = torch.zeros(od.k_cache.shape, dtype=torch.uint8, device="cuda")
+        P.pa_decode_fp8(out, od.q, codes, codes, od.tables, od.ctx, other.scale, 1.0, 1.0, 16, 2,
+                        max_context_len=other.max_context_len)
+        P.pa_decode_fp8_append(out, od.q, od.new_k, od.new_v, codes, codes.clone(), od.tables, od.ctx,
+                               other.scale, 1.0, 1.0, 16, 2, max_context_len=other.max_context_len)
+        if D == 64:
+            G.decode(other, G.to_device(other))
+    torch.cuda.synchronize()
+    kv = P.DenseKV(case.num_seqs, 3000, 8, 128)
+    kv.step(case.context_lens.tolist())
+    _fill(kv, case)
+    assert _dense_decode(kv, case).tobytes() == paged.tobytes()
+    kv.close()
