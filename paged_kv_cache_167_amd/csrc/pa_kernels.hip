@@ -1798,6 +1798,14 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 // that cross one of those limits.
 // ---------------------------------------------------------------------------
 
+// max(a, b, c) in one instruction.  fmaxf would first quieten each operand that is not
+// known to be a quiet NaN (the products' outputs are not), one extra instruction per value.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 constexpr int kPfWaves = 4;                            // waves per work-group
 constexpr int kPfInterleave = 2;                       // blocks whose score products interleave
 constexpr int kPfKeys = 32;                            // keys per tile
@@ -2052,26 +2060,30 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   }
 
   // Softmax of block nr over the tile, then its P.V products; unmasked: no key of the tile
-  // lies past any row's limit.  (Separate code for unmasked tiles was measured slower: it
-  // raises register pressure more than it saves.)
-  auto block_pv = [&](auto nrc, int key_base, bool unmasked, const f32x4 (&sc)[2],
+  // lies past any row's limit (wave-uniform), so interior tiles skip the masking.  A masked
+  // score becomes -inf, whose exp2 is 0: every row sees key 0 (its limit is at least 0), so
+  // from the first tile on its reference maximum is finite.
+  auto block_pv = [&](auto nrc, int key_base, bool unmasked, const f32x4 (&scr)[2],
                       const f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
     constexpr int nr = decltype(nrc)::value;
     constexpr float kRebase = 8.0f;
-    bool ok[2][4];
-    float mt = -INFINITY;
+    f32x4 sc[2] = {scr[0], scr[1]};
+    if (!unmasked) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
+      for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ok[kh][i] = unmasked || (key_base + 16 * kh + 4 * jq + i <= lim[nr]);
-        mt = fmaxf(mt, ok[kh][i] ? sc[kh][i] : -INFINITY);
-      }
+        for (int i = 0; i < 4; ++i)
+          sc[kh][i] = key_base + 16 * kh + 4 * jq + i <= lim[nr] ? sc[kh][i] : -INFINITY;
+    }
+    float mt = max3f(sc[0][0], sc[0][1], sc[0][2]);
+    mt = max3f(mt, sc[0][3], sc[1][0]);
+    mt = max3f(mt, sc[1][1], sc[1][2]);
+    mt = max3f(mt, sc[1][3], sc[1][3]);
     {
       const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
-      mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
+      mt = max3f(as_f(x32[0]), as_f(x32[1]), as_f(x32[1]));
       const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
-      mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
+      mt = max3f(as_f(x16[0]), as_f(x16[1]), as_f(x16[1]));
     }
     mt *= a.scale_log2;
     if (__builtin_amdgcn_ballot_w64(mt > m[nr] + kRebase) != 0) {
@@ -2087,7 +2099,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[kh][i] = ok[kh][i] ? __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr])) : 0.0f;
+        p[kh][i] = __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr]));
         l[nr] += p[kh][i];
       }
     const f16x8 pb = {static_cast<f16>(p[0][0]), static_cast<f16>(p[0][1]), static_cast<f16>(p[0][2]),
