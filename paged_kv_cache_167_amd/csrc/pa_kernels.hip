@@ -1798,6 +1798,19 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 // that cross one of those limits.
 // ---------------------------------------------------------------------------
 
+// Chunk position of chunk 0 of key row r (mod 16) in the prefill ring: chunk c is stored at
+// c ^ pf_swz(r).  D = 128 rows are 256 bytes, a full sweep of the LDS banks.  pf_swz is a
+// permutation of 0..15, so the 16 rows a 16-lane quarter of a ds_read_b128 reads (one chunk
+// each) land on 16 distinct positions; and the transposing V reads, 2 adjacent chunks of 4
+// rows per 16 lanes, cover 8 distinct positions per 4-row group and all 16 over rows 0-7
+// (and 8-15), conflict-free whether the LDS serves 16 or 32 lanes of them per cycle.
+// D = 64 rows are 128 bytes: swz already keeps even rows, and odd rows, apart.
+template <int D>
+__device__ __forceinline__ int pf_swz(int r) {
+  if constexpr (D == 128) return 2 * (r & 3) + 8 * ((r >> 2) & 1) + ((r >> 3) & 1);
+  return swz(r);
+}
+
 // max(a, b, c) in one instruction.  fmaxf would first quieten each operand that is not
 // known to be a quiet NaN (the products' outputs are not), one extra instruction per value.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -1997,21 +2010,21 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   uint32_t ka[KB], va[NB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
-    ka[kb] = ring + static_cast<uint32_t>(g * ROW + (((jq * KB + kb) ^ swz(g)) * 16));
+    ka[kb] = ring + static_cast<uint32_t>(g * ROW + (((jq * KB + kb) ^ pf_swz<D>(g)) * 16));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = 4 * jq + (g >> 2), qq = g & 3;
     const int c = 2 * nb + (qq >> 1);
-    va[nb] = ring + static_cast<uint32_t>(TILE + r * ROW + ((c ^ swz(r)) * 16) + (qq & 1) * 8);
+    va[nb] = ring + static_cast<uint32_t>(TILE + r * ROW + ((c ^ pf_swz<D>(r)) * 16) + (qq & 1) * 8);
   }
   // loads: wave w brings key rows 8 w .. 8 w + 7 of each tile; load i, lane l fills LDS
-  // position 64 i + l of that run (row rr, chunk position p, holding chunk p ^ swz(row))
+  // position 64 i + l of that run (row rr, chunk position p, holding chunk p ^ pf_swz(row))
   uint32_t lo[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pos = i * 64 + lane;
     const int rr = pos / NC, pp = pos % NC;
-    lo[i] = static_cast<uint32_t>(rr * ROW + ((pp ^ swz((C::kWaveRows * w + rr) & 15)) * 16));
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((pp ^ pf_swz<D>((C::kWaveRows * w + rr) & 15)) * 16));
   }
   const int bsz = a.block_size;
   const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
