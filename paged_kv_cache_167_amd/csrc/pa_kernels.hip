@@ -910,6 +910,19 @@ struct MCfg {
 // x 2 chunks) do too.
 __device__ __forceinline__ int swz(int r) { return (2 * r + (r >> 2)) & 7; }
 
+// Chunk position of chunk 0 of key row r (mod 16) in a ring of 256-byte rows: chunk c is stored
+// at c ^ swz16(r).  D = 128 rows are 256 bytes, a full sweep of the LDS banks.  swz16 is a
+// permutation of 0..15, so the 16 rows a 16-lane quarter of a ds_read_b128 reads (one chunk
+// each) land on 16 distinct positions; and the transposing V reads, 2 adjacent chunks of 4
+// rows per 16 lanes, cover 8 distinct positions per 4-row group and all 16 over rows 0-7
+// (and 8-15), conflict-free whether the LDS serves 16 or 32 lanes of them per cycle.
+// D = 64 rows are 128 bytes: swz already keeps even rows, and odd rows, apart.
+template <int D>
+__device__ __forceinline__ int swz16(int r) {
+  if constexpr (D == 128) return 2 * (r & 3) + 8 * ((r >> 2) & 1) + ((r >> 3) & 1);
+  return swz(r);
+}
+
 // A wave-uniform pointer, forced into SGPRs (an asm "s" operand needs it there).
 template <typename T>
 __device__ __forceinline__ const T* uniform_ptr(const T* p) {
@@ -1358,19 +1371,19 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {  // lane (g = token, jq) takes chunk jq * KB + kb of row g
       const int c = jq * KB + kb;
-      ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz(g)) * 16));
+      ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz16<D>(g)) * 16));
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {  // lane 16 jq + 4 i + q: row 4 jq + i, dims 16 nb + 4 q
       const int r = 4 * jq + (g >> 2), q = g & 3;
       const int c = 2 * nb + (q >> 1);
-      va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz(r)) * 16) + (q & 1) * 8);
+      va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz16<D>(r)) * 16) + (q & 1) * 8);
     }
   }
   // q operand: lane (g, jq) reads chunks jq * KB .. jq * KB + KB - 1 of q row g
   const uint32_t qa = ring + static_cast<uint32_t>(g * ROWQ + jq * KB * 16);
   // load i, lane l fills LDS position 64 i + l of a half: row r, chunk position p, which
-  // holds chunk p ^ swz(r) of the row; lo[i] is its byte offset from the row slot start,
+  // holds chunk p ^ swz16(r) of the row; lo[i] is its byte offset from the row slot start,
   // hi8[i] whether the row is in the second half of the tile
   const int bsz = a.block_size;
   uint32_t lo[LOADS];
@@ -1382,7 +1395,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     const int pos = i * 64 + lane;
     const int r = pos / NC, p = pos % NC;
     const int rr = bsz >= TK ? r : (r & (bsz - 1));  // row within its block
-    const int sw = F8 ? swz8<D>(r) : swz(r);
+    const int sw = F8 ? swz8<D>(r) : swz16<D>(r);
     row_of[i] = r;
     chunk_of[i] = static_cast<uint32_t>((p ^ sw) * 16);
     // contiguous cache: consecutive tokens of one head are token_bytes apart
@@ -1798,19 +1811,6 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 // that cross one of those limits.
 // ---------------------------------------------------------------------------
 
-// Chunk position of chunk 0 of key row r (mod 16) in the prefill ring: chunk c is stored at
-// c ^ pf_swz(r).  D = 128 rows are 256 bytes, a full sweep of the LDS banks.  pf_swz is a
-// permutation of 0..15, so the 16 rows a 16-lane quarter of a ds_read_b128 reads (one chunk
-// each) land on 16 distinct positions; and the transposing V reads, 2 adjacent chunks of 4
-// rows per 16 lanes, cover 8 distinct positions per 4-row group and all 16 over rows 0-7
-// (and 8-15), conflict-free whether the LDS serves 16 or 32 lanes of them per cycle.
-// D = 64 rows are 128 bytes: swz already keeps even rows, and odd rows, apart.
-template <int D>
-__device__ __forceinline__ int pf_swz(int r) {
-  if constexpr (D == 128) return 2 * (r & 3) + 8 * ((r >> 2) & 1) + ((r >> 3) & 1);
-  return swz(r);
-}
-
 // max(a, b, c) in one instruction.  fmaxf would first quieten each operand that is not
 // known to be a quiet NaN (the products' outputs are not), one extra instruction per value.
 __device__ __forceinline__ float max3f(float a, float b, float c) {
@@ -1956,7 +1956,9 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   __shared__ __align__(1024) char s_ring[NST * STAGE];
   __shared__ int s_bad;
 
-  const int w = threadIdx.x / kWave;  // wave in the work-group
+  // wave in the work-group, known uniform: what depends only on it and the tile (table
+  // entries, load bases) is scalar work
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
   const int g = lane % 16, jq = lane / 16;
   const int rb = a.n_row_blocks - 1 - static_cast<int>(blockIdx.x);  // longest blocks first
@@ -2010,21 +2012,21 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   uint32_t ka[KB], va[NB];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
-    ka[kb] = ring + static_cast<uint32_t>(g * ROW + (((jq * KB + kb) ^ pf_swz<D>(g)) * 16));
+    ka[kb] = ring + static_cast<uint32_t>(g * ROW + (((jq * KB + kb) ^ swz16<D>(g)) * 16));
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int r = 4 * jq + (g >> 2), qq = g & 3;
     const int c = 2 * nb + (qq >> 1);
-    va[nb] = ring + static_cast<uint32_t>(TILE + r * ROW + ((c ^ pf_swz<D>(r)) * 16) + (qq & 1) * 8);
+    va[nb] = ring + static_cast<uint32_t>(TILE + r * ROW + ((c ^ swz16<D>(r)) * 16) + (qq & 1) * 8);
   }
   // loads: wave w brings key rows 8 w .. 8 w + 7 of each tile; load i, lane l fills LDS
-  // position 64 i + l of that run (row rr, chunk position p, holding chunk p ^ pf_swz(row))
+  // position 64 i + l of that run (row rr, chunk position p, holding chunk p ^ swz16(row))
   uint32_t lo[LOADS];
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
     const int pos = i * 64 + lane;
     const int rr = pos / NC, pp = pos % NC;
-    lo[i] = static_cast<uint32_t>(rr * ROW + ((pp ^ pf_swz<D>((C::kWaveRows * w + rr) & 15)) * 16));
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((pp ^ swz16<D>((C::kWaveRows * w + rr) & 15)) * 16));
   }
   const int bsz = a.block_size;
   const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
@@ -2038,25 +2040,26 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
     const int key0 = f * kPfKeys + C::kWaveRows * w;
     return uniform_ptr(key0 < kend ? trow + (key0 >> a.log2_block) : a.block_tables);
   };
-  bool bad = false;
+  int bad = 0;  // uniform: a table entry of this wave's rows lay outside the pool
   auto fetch = [&](int f, int st, int p) __attribute__((always_inline)) {
     const int key0 = f * kPfKeys + C::kWaveRows * w;
     const bool real = key0 < kend;  // phantom tiles and rows past the context read block 0
-    if (real && (p < 0 || p >= a.num_blocks)) {
-      bad = true;
-      p = 0;
-    }
-    if (!real) p = 0;
+    p = __builtin_amdgcn_readfirstlane(p);  // a scalar load's result: uniform
+    const bool outside = real && (p < 0 || p >= a.num_blocks);
+    bad |= outside ? 1 : 0;
+    if (outside || !real) p = 0;
     const uint64_t base = static_cast<uint64_t>(static_cast<uint32_t>(p)) * block_bytes +
                           static_cast<uint64_t>(kvh) * head_bytes +
                           static_cast<uint64_t>(real ? (key0 & (bsz - 1)) : 0) * ROW;
     char* dst = s_ring + st * STAGE + C::kWaveRows * w * ROW;
+    const char* kb = uniform_ptr(kcache + base);  // scalar bases, 32-bit per-lane offsets
+    const char* vb = uniform_ptr(vcache + base);
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
       // (explicit casts: without them the host pass of this compiler drops the kernel)
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kcache + base + lo[i]),
-                                       static_cast<void*>(dst + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vcache + base + lo[i]),
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(kb + lo[i]), static_cast<void*>(dst + i * 1024), 16,
+                                       0, 0);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(vb + lo[i]),
                                        static_cast<void*>(dst + TILE + i * 1024), 16, 0, 0);
     }
   };
