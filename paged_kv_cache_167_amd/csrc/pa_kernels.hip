@@ -1862,7 +1862,9 @@ struct PCfg {
 // Stage read of the prefill ring, D = 128: issue the scalar load of the next table entry,
 // wait for this wave's loads of the stage, meet the other waves at the barrier (their
 // loads have landed and none still reads the stage to be refilled next), then read the K
-// operands of both key halves (the second half is 16 rows further) and the V^T operands.
+// operands of both key halves (the second half is 16 rows further), and issue the V^T
+// reads without waiting for them: they land while the score products run, and
+// pf_wait_v_d128 waits for them before the V operands are used.
 template <int VM, int OFF, int ROW>
 __device__ __forceinline__ void pf_read_d128(const uint32_t (&ka)[4], const uint32_t (&va)[8],
                                              f16x8 (&k)[2][4], f16x4 (&v)[2][8], const int32_t* e,
@@ -1902,8 +1904,7 @@ __device__ __forceinline__ void pf_read_d128(const uint32_t (&ka)[4], const uint
       "ds_read_b64_tr_b16 %[v14], %[va4] offset:%[o1]\n\t"
       "ds_read_b64_tr_b16 %[v15], %[va5] offset:%[o1]\n\t"
       "ds_read_b64_tr_b16 %[v16], %[va6] offset:%[o1]\n\t"
-      "ds_read_b64_tr_b16 %[v17], %[va7] offset:%[o1]\n\t"
-      "s_waitcnt lgkmcnt(0)"
+      "ds_read_b64_tr_b16 %[v17], %[va7] offset:%[o1]"
       : [v00] "=&v"(v[0][0]), [v01] "=&v"(v[0][1]), [v02] "=&v"(v[0][2]), [v03] "=&v"(v[0][3]),
         [v04] "=&v"(v[0][4]), [v05] "=&v"(v[0][5]), [v06] "=&v"(v[0][6]), [v07] "=&v"(v[0][7]),
         [v10] "=&v"(v[1][0]), [v11] "=&v"(v[1][1]), [v12] "=&v"(v[1][2]), [v13] "=&v"(v[1][3]),
@@ -1911,6 +1912,19 @@ __device__ __forceinline__ void pf_read_d128(const uint32_t (&ka)[4], const uint
       : [va0] "v"(va[0]), [va1] "v"(va[1]), [va2] "v"(va[2]), [va3] "v"(va[3]), [va4] "v"(va[4]),
         [va5] "v"(va[5]), [va6] "v"(va[6]), [va7] "v"(va[7]), [o0] "n"(OFF), [o1] "n"(OFF + 16 * ROW)
       : "memory");
+}
+
+// The V^T reads pf_read_d128 issued have landed: the 16 registers they write are in-out
+// operands, so nothing reads them before this wait.  The score accumulators are inputs, so
+// that every score product (they need no V) is issued before it; being inputs only, the
+// products stay their last writers and the usual wait states before reading them hold.
+__device__ __forceinline__ void pf_wait_v_d128(f16x4 (&v)[2][8], const f32x4 (&s)[4]) {
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(v[0][0]), "+v"(v[0][1]), "+v"(v[0][2]), "+v"(v[0][3]), "+v"(v[0][4]), "+v"(v[0][5]),
+                 "+v"(v[0][6]), "+v"(v[0][7]), "+v"(v[1][0]), "+v"(v[1][1]), "+v"(v[1][2]), "+v"(v[1][3]),
+                 "+v"(v[1][4]), "+v"(v[1][5]), "+v"(v[1][6]), "+v"(v[1][7])
+               : "v"(s[0]), "v"(s[1]), "v"(s[2]), "v"(s[3])
+               : "memory");
 }
 
 template <int VM, int OFF, int ROW>
@@ -2064,16 +2078,20 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
     }
   };
 
-  // ---- softmax state and accumulators
-  f32x4 o[NR][NB];
-  float m[NR], l[NR];
+  // ---- softmax state and accumulators.  The row sums come from the matrix cores as well:
+  // ones^T P^T puts sum_k p(q, k) (of the fp16 probabilities the P.V product uses) in every
+  // element of lane (q, .), one product per block and tile instead of 8 additions per lane.
+  f32x4 o[NR][NB], lsum[NR];
+  float m[NR];
 #pragma unroll
   for (int nr = 0; nr < NR; ++nr) {
     m[nr] = -INFINITY;
-    l[nr] = 0.0f;
+    lsum[nr] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nr][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   }
+  const f16 one = static_cast<f16>(1.0f);
+  const f16x8 ones = {one, one, one, one, one, one, one, one};
 
   // Softmax of block nr over the tile, then its P.V products; unmasked: no key of the tile
   // lies past any row's limit (wave-uniform), so interior tiles skip the masking.  A masked
@@ -2105,7 +2123,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
     if (__builtin_amdgcn_ballot_w64(mt > m[nr] + kRebase) != 0) {
       const float m_new = fmaxf(m[nr], mt);
       const float corr = rescale(m[nr], m_new);
-      l[nr] *= corr;
+      lsum[nr] *= corr;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) o[nr][nb] *= corr;
       m[nr] = m_new;
@@ -2114,13 +2132,11 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[kh][i] = __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr]));
-        l[nr] += p[kh][i];
-      }
+      for (int i = 0; i < 4; ++i) p[kh][i] = __builtin_amdgcn_exp2f(fmaf(sc[kh][i], a.scale_log2, -m[nr]));
     const f16x8 pb = {static_cast<f16>(p[0][0]), static_cast<f16>(p[0][1]), static_cast<f16>(p[0][2]),
                       static_cast<f16>(p[0][3]), static_cast<f16>(p[1][0]), static_cast<f16>(p[1][1]),
                       static_cast<f16>(p[1][2]), static_cast<f16>(p[1][3])};
+    lsum[nr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pb, lsum[nr], 0, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const f16x8 vt = {vop[0][nb][0], vop[0][nb][1], vop[0][nb][2], vop[0][nb][3],
@@ -2131,21 +2147,6 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
 
   auto consume = [&](int f, const f16x8 (&kop)[2][KB], f16x4 (&vop)[2][NB]) __attribute__((always_inline)) {
     const int key_base = f * kPfKeys;
-    if (key_base + kPfKeys > kend) {  // V rows at or past kend (poison, or block 0) must not reach O
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        uint32_t mlo = 0u, mhi = 0u;
-        const int k0 = key_base + 16 * kh + 4 * jq;
-        mlo |= (k0 + 0 < kend) ? 0x0000FFFFu : 0u;
-        mlo |= (k0 + 1 < kend) ? 0xFFFF0000u : 0u;
-        mhi |= (k0 + 2 < kend) ? 0x0000FFFFu : 0u;
-        mhi |= (k0 + 3 < kend) ? 0xFFFF0000u : 0u;
-        const uint64_t msk = (static_cast<uint64_t>(mhi) << 32) | mlo;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          vop[kh][nb] = __builtin_bit_cast(f16x4, __builtin_bit_cast(uint64_t, vop[kh][nb]) & msk);
-      }
-    }
     // uniform: no key of the tile lies past any row's limit
     const bool unmasked = key_base + kPfKeys - 1 <= wave_min_lim;
     // blocks in groups of NI: the scores of a group with the dim chunk outermost, so its
@@ -2164,6 +2165,28 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
 #pragma unroll
           for (int kh = 0; kh < 2; ++kh)
             sc[b][kh] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kh][kb], qop[g0 + b][kb], sc[b][kh], 0, 0, 0);
+      if constexpr (g0 == 0) {
+        if constexpr (D == 128) {  // the V^T reads have landed, after the score products
+          static_assert(NI == 2, "the wait holds the score chains of two blocks");
+          const f32x4 s4[4] = {sc[0][0], sc[0][1], sc[1][0], sc[1][1]};
+          pf_wait_v_d128(vop, s4);
+        }
+        if (key_base + kPfKeys > kend) {  // V rows at or past kend (poison, or block 0) must not reach O
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) {
+            uint32_t mlo = 0u, mhi = 0u;
+            const int k0 = key_base + 16 * kh + 4 * jq;
+            mlo |= (k0 + 0 < kend) ? 0x0000FFFFu : 0u;
+            mlo |= (k0 + 1 < kend) ? 0xFFFF0000u : 0u;
+            mhi |= (k0 + 2 < kend) ? 0x0000FFFFu : 0u;
+            mhi |= (k0 + 3 < kend) ? 0xFFFF0000u : 0u;
+            const uint64_t msk = (static_cast<uint64_t>(mhi) << 32) | mlo;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              vop[kh][nb] = __builtin_bit_cast(f16x4, __builtin_bit_cast(uint64_t, vop[kh][nb]) & msk);
+          }
+        }
+      }
       unroll<NI>([&](auto bc) __attribute__((always_inline)) {
         constexpr int b = decltype(bc)::value;
         block_pv(std::integral_constant<int, g0 + b>{}, key_base, unmasked, sc[b], vop);
@@ -2208,13 +2231,7 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   // ---- rows: o / l, or NaN when a table entry was outside the pool
 #pragma unroll
   for (int nr = 0; nr < NR; ++nr) {
-    float lt = l[nr];
-    {
-      const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(lt), as_u(lt), false, false);
-      lt = as_f(x32[0]) + as_f(x32[1]);
-      const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(lt), as_u(lt), false, false);
-      lt = as_f(x16[0]) + as_f(x16[1]);
-    }
+    const float lt = lsum[nr][0];  // the whole row's sum, in every lane of the row
     if (!rvalid[nr]) continue;
     const int r = row_lo + 16 * NR * w + 16 * nr + g;
     const float inv = any_bad ? __builtin_nanf("") : 1.0f / lt;
