@@ -1062,13 +1062,15 @@ __device__ __forceinline__ void read_stage_mf(const uint32_t (&ka)[D / 32], cons
 // Token of a tile held in score row i (the K row lane g reads is tau(g)).
 __device__ __forceinline__ int tau(int i) { return (i >> 2) + 4 * (i & 3); }
 
-// Chunk c of E4M3 row r is stored at chunk position c ^ swz8<D>(r).  The 8 lanes of one
-// ds_read_b128 cycle read rows tau(0..7) or tau(8..15) at one chunk; for D = 128 (8
-// chunks a row) swz8 takes 8 distinct values over either set, for D = 64 (4 chunks, two
-// rows per 128 bytes) 4 distinct values over its even and over its odd rows.
+// Chunk c of E4M3 row r is stored at chunk position c ^ swz8<D>(r).  A 16-lane quarter of
+// a ds_read_b128 reads one chunk of all 16 rows of a tile.  D = 128 rows are 128 bytes, so
+// even rows fall on one half of the 64 banks and odd rows on the other: swz8 takes 8
+// distinct values over the even rows and over the odd rows (and over rows tau(0..7) and
+// tau(8..15), the rows 8 lanes read together).  D = 64 rows are 64 bytes, a quarter of the
+// banks each: swz8 takes 4 distinct values over the rows of each quarter.
 template <int D>
 __device__ __forceinline__ int swz8(int r) {
-  return D == 128 ? ((r >> 2) | ((r & 1) << 2)) : ((r >> 2) & 3);
+  return D == 128 ? (((r >> 1) & 7) ^ (r & 1)) : ((r >> 2) & 3);
 }
 
 // Four E4M3 codes (byte i = element i) as fp16, exactly.
