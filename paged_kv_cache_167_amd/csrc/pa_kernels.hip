@@ -1846,6 +1846,7 @@ struct PrefillArgs {
   int max_context_len;
   int64_t num_blocks;
   int n_row_blocks;  // work-groups per (sequence, kv head)
+  int rb_outer;      // grid (kv head, sequence, row block) instead of (row block, kv head, sequence)
 };
 
 template <int D>
@@ -1977,9 +1978,12 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
   const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
   const int lane = threadIdx.x % kWave;
   const int g = lane % 16, jq = lane / 16;
-  const int rb = a.n_row_blocks - 1 - static_cast<int>(blockIdx.x);  // longest blocks first
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  // work-groups start in grid order as compute units free up; the longest row blocks (the
+  // last of each chunk) come first, within each (sequence, kv head) or, with rb_outer, over
+  // the whole grid
+  const int rb = a.n_row_blocks - 1 - static_cast<int>(a.rb_outer ? blockIdx.z : blockIdx.x);
+  const int kvh = a.rb_outer ? blockIdx.x : blockIdx.y;
+  const int s = a.rb_outer ? blockIdx.y : blockIdx.z;
   const int G = a.group;
 
   // every value below is uniform over the work-group
@@ -2712,12 +2716,19 @@ int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, v
 
 bool valid_scale(float x) { return x > 0.0f && std::isfinite(x); }
 
+// Grid order.  When chunks make up at least half their context (whole prompts), the causal
+// row blocks differ most in length: row blocks outermost starts the longest ones of every
+// sequence and head first, which balances the compute units (Llama-2-70B prompts: 12 %
+// faster).  After a long cached prefix the blocks differ less, and keeping the row blocks of
+// one (sequence, kv head) together, which share its K/V in the caches, is faster (7 %).
 template <int D, int NR>
 int launch_prefill_rows(PrefillArgs a, int64_t rows, int num_seqs, hipStream_t stream) {
   constexpr int kRows = kPfWaves * NR * 16;
   a.n_row_blocks = static_cast<int>((rows + kRows - 1) / kRows);
-  hipLaunchKernelGGL((pa_prefill_kernel<D, NR, kPfStages>), dim3(a.n_row_blocks, a.num_kv_heads, num_seqs),
-                     dim3(kPfWaves * kWave), 0, stream, a);
+  a.rb_outer = 2 * static_cast<int64_t>(a.max_query_len) >= a.max_context_len && a.n_row_blocks <= 65535 ? 1 : 0;
+  const dim3 grid = a.rb_outer ? dim3(a.num_kv_heads, num_seqs, a.n_row_blocks)
+                               : dim3(a.n_row_blocks, a.num_kv_heads, num_seqs);
+  hipLaunchKernelGGL((pa_prefill_kernel<D, NR, kPfStages>), grid, dim3(kPfWaves * kWave), 0, stream, a);
   return check_hip("pa_prefill_kernel launch");
 }
 
