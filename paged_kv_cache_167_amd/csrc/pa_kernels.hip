@@ -2252,8 +2252,8 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
 }
 
 // ---------------------------------------------------------------------------
-// decode, second launch (pa_decode_reduce only; pa_decode merges in its one launch): one
-// wave per (sequence, query head).  Empty or invalid contexts get their zero or NaN row
+// decode, second launch (of every decode call, or pa_decode_reduce alone): one wave per
+// (sequence, query head).  Empty or invalid contexts get their zero or NaN row
 // here; a segment held whole by one wave was written by it; a segment split over waves
 // w0..w1 is merged from the tail record of w0 and the head records of w0+1..w1.
 // ---------------------------------------------------------------------------

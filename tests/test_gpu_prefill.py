@@ -117,10 +117,14 @@ def test_small_shapes(D, B, hq, hkv, ctx, qlen):
     _check(got, ref, case, label)
 
 
-def test_poscode_rows_see_exactly_their_prefix():
+# chunks after a cached prefix, and whole prompts (which the host launches with the row
+# blocks outermost in the grid)
+@pytest.mark.parametrize("ctx,qlen", [([700, 300], [300, 300]), ([300, 260, 300], [300, 260, 200])])
+def test_poscode_rows_see_exactly_their_prefix(ctx, qlen):
     """V coordinate 0 carries position / max ctx: a row that saw a key past its position, or
     missed part of its prefix, moves that coordinate far outside the tolerance."""
-    case = W.make_prefill_case(seed=5, dtype=np.float16, context_lens=[700, 300], query_lens=[300, 300],
+    G.say(f"prefill poscode ctx {ctx} n {qlen}")
+    case = W.make_prefill_case(seed=5, dtype=np.float16, context_lens=ctx, query_lens=qlen,
                                num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
                                sigma=0.5, variant="poscode")
     d = _to_device(case)
