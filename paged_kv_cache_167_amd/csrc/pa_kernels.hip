@@ -455,6 +455,8 @@ struct Work {
   int S, max_ctx, n_units;
   int Q, R;     // every wave takes Q tiles, the first R waves one more
   int A, n_my;  // this wave's share: tiles [A, A + n_my)
+  int ctx0;     // this lane's context length among the first 64 sequences (0 past S): one
+                // load serves the total, the scan and the cursor
 
   __device__ int seg_tiles(int ctx) const {  // invalid or empty contexts contribute no tiles
     return (ctx > 0 && ctx <= max_ctx) ? (ctx + TK - 1) / TK : 0;
@@ -465,8 +467,9 @@ struct Work {
     S = a.num_seqs;
     max_ctx = a.max_context_len;
     n_units = a.n_units;
-    int part = 0;
-    for (int b = 0; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
+    ctx0 = lane < S ? ctxs[lane] : 0;
+    int part = seg_tiles(ctx0);
+    for (int b = kWave; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
     const int total = wave_sum_int(part) * n_units;
     Q = total / a.num_waves;
     R = total - Q * a.num_waves;
@@ -482,13 +485,18 @@ struct Work {
   // Cursor at tile A: scan the per-sequence tile counts for the sequence covering it.
   __device__ Cursor locate(int lane) const {
     int s0 = 0, base = 0;  // base: global index of s0's first tile
+    int cx = 0;            // context length of s0
+    bool found = false;
     for (int b = 0; b < S; b += kWave) {
-      const int ts = ((b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0) * n_units;
+      const int cl = b == 0 ? ctx0 : ((b + lane < S) ? ctxs[b + lane] : 0);
+      const int ts = seg_tiles(cl) * n_units;
       const int incl = wave_incl_scan_int(ts, lane);
       const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > A);
       if (hit != 0) {
         const int l = __builtin_ctzll(hit);
         s0 = b + l;
+        cx = __builtin_amdgcn_readlane(cl, l);
+        found = true;
         base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
         break;
       }
@@ -496,7 +504,7 @@ struct Work {
     }
     Cursor c;
     c.s = s0;
-    c.ctx = scalar_load(ctxs + s0);
+    c.ctx = found ? cx : scalar_load(ctxs + s0);
     c.nt = seg_tiles(c.ctx);
     c.unit = (A - base) / c.nt;
     c.t = (A - base) - c.unit * c.nt;
