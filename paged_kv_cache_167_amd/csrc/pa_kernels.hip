@@ -43,6 +43,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -2450,10 +2451,12 @@ int check_decode(const DecodeCall& c, Geom* g) {
   if (c.num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", c.num_seqs);
   *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size,
                 c.dtype);
-  // tile counts are 32-bit in the kernel (a tile holds at least 8 tokens)
-  if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8) >
+  // tile counts and segment indexes are 32-bit in the kernels (a tile holds at least 8
+  // tokens; every segment counts as at least one tile, since the reduce indexes all of them)
+  if (static_cast<int64_t>(c.num_seqs) * g->n_units *
+          std::max<int64_t>(1, (static_cast<int64_t>(c.max_context_len) + 7) / 8) >
       (static_cast<int64_t>(1) << 31) - 1)
-    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles");
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
   if (c.num_blocks > (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "num_blocks above 2^31 - 1");
   if (static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.kv_fp8 ? 1 : c.dtype == PA_F16 ? 2 : 4) >
@@ -2857,6 +2860,8 @@ int pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
   if (num_seqs == 0) return PA_OK;
   const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, dtype);
+  if (static_cast<int64_t>(num_seqs) * g.n_units > (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 segments");
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(out, 16) || !aligned(context_lens, 4)) return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);

@@ -100,6 +100,8 @@ def _decode(**over):
     (dict(ws=None), _lib.PA_ERR_WORKSPACE),
     (dict(wsb=16), _lib.PA_ERR_WORKSPACE),
     (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),     # not 256-byte aligned
+    # more than 2^31 - 1 segments (sequence x kv head), even with empty contexts
+    (dict(S=65535, hkv=40000, hq=40000, D=64, B=8, mcl=0, wsb=1 << 50), _lib.PA_ERR_INVALID_ARG),
 ])
 def test_decode_rejects_bad_arguments(over, code):
     assert _decode(**over) == code
@@ -144,6 +146,9 @@ def test_reduce_rejects_bad_arguments():
     assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 4096, 0, 1, None, 0, None) == \
         _lib.PA_ERR_WORKSPACE
     assert lib.pa_decode_reduce(FAKE, FAKE, 4, 30, 8, 128, 4096, 0, 1, FAKE, 1 << 30, None) == \
+        _lib.PA_ERR_INVALID_ARG
+    # more than 2^31 - 1 segments (sequence x kv head), whatever the workspace
+    assert lib.pa_decode_reduce(FAKE, FAKE, 65535, 40000, 40000, 64, 0, 0, 1, FAKE, 1 << 50, None) == \
         _lib.PA_ERR_INVALID_ARG
     assert lib.pa_decode_reduce(FAKE, FAKE, 0, 32, 8, 128, 4096, 0, 1, None, 0, None) == _lib.PA_OK
 
