@@ -72,7 +72,9 @@ extern "C" {
  * k, v              device, [num_tokens, num_kv_heads, head_dim], dtype
  * slot_mapping      device, [num_tokens] int64
  * k_cache, v_cache  device, [num_blocks, num_kv_heads, block_size, head_dim], dtype; updated in place
- * num_tokens        >= 0 (0 launches nothing)
+ * num_tokens        >= 0 (0 launches nothing); num_tokens * num_kv_heads * head_dim * element
+ *                   size / 16 at most 2^31 - 256 per call (one thread per 16-byte chunk; a
+ *                   larger write is refused: split the tokens)
  * returns PA_OK, or a negative code with nothing launched.
  */
 int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
@@ -216,7 +218,8 @@ int pa_decode_append_partitions(void* out, const void* q, const void* k_new, con
  * is stored as the code nearest to y = x * (1/k_scale), where 1/k_scale is rounded once
  * to fp32 and y is one fp32 product; ties go to the even code, |y| beyond 448 saturates
  * to +-448 (code 0x7E / 0xFE), any NaN gives 0x7F.  Same for v with v_scale.
- * Slot handling, skips and races are those of pa_cache_write.
+ * Slot handling, skips and races are those of pa_cache_write; num_tokens * num_kv_heads *
+ * head_dim / 16 is at most 2^31 - 256 per call (one thread per 16 codes).
  *
  * k, v              device, [num_tokens, num_kv_heads, head_dim] fp16
  * k_cache, v_cache  device, [num_blocks, num_kv_heads, block_size, head_dim] uint8; updated in place

@@ -2698,12 +2698,19 @@ int dispatch(const DecodeCall& c, const Geom& g) {
   return c.head_dim == 64 ? dispatch_f32<Which, 64>(c, g) : dispatch_f32<Which, 128>(c, g);
 }
 
+// A launch's work-items are counted in 32 bits: one thread per 16-byte chunk (fp16/fp32
+// pools) or per 16 codes (E4M3 pools), in whole work-groups of 256.
+constexpr int64_t kMaxWriteThreads = (static_cast<int64_t>(1) << 31) - 256;
+
 template <typename T, int D>
 int launch_cache_write(const void* k, const void* v, const int64_t* slots, void* kc, void* vc,
                        int num_tokens, int num_kv_heads, int block_size, int64_t num_blocks,
                        hipStream_t stream) {
   constexpr int kChunksPerRow = D * static_cast<int>(sizeof(T)) / 16;
   const int64_t chunks = static_cast<int64_t>(num_tokens) * num_kv_heads * kChunksPerRow;
+  if (chunks > kMaxWriteThreads)
+    return fail(PA_ERR_INVALID_ARG, "%lld 16-byte chunks in one write; at most %lld (split the tokens)",
+                (long long)chunks, (long long)kMaxWriteThreads);
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL((pa_cache_write_kernel<T, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const T*>(k), static_cast<const T*>(v), slots,
@@ -2717,6 +2724,9 @@ int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, v
                            float k_inv, float v_inv, int num_tokens, int num_kv_heads, int block_size,
                            int64_t num_blocks, hipStream_t stream) {
   const int64_t chunks = static_cast<int64_t>(num_tokens) * num_kv_heads * (D / 16);
+  if (chunks > kMaxWriteThreads)
+    return fail(PA_ERR_INVALID_ARG, "%lld threads in one write; at most %lld (split the tokens)",
+                (long long)chunks, (long long)kMaxWriteThreads);
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL((pa_cache_write_fp8_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const f16*>(k), static_cast<const f16*>(v), slots,

@@ -130,6 +130,7 @@ def _write(**over):
     (dict(k=None), _lib.PA_ERR_INVALID_ARG),
     (dict(kc=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
     (dict(sm=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
+    (dict(T=(1 << 31) - 1), _lib.PA_ERR_INVALID_ARG),  # more threads than one launch counts
 ])
 def test_cache_write_rejects_bad_arguments(over, code):
     assert _write(**over) == code
@@ -273,6 +274,7 @@ def _write_fp8(**over):
     (dict(v=None), _lib.PA_ERR_INVALID_ARG),
     (dict(vc=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
     (dict(sm=FAKE + 4), _lib.PA_ERR_INVALID_ARG),
+    (dict(T=(1 << 31) - 1), _lib.PA_ERR_INVALID_ARG),  # more threads than one launch counts
 ])
 def test_cache_write_fp8_rejects_bad_arguments(over, code):
     assert _write_fp8(**over) == code
