@@ -126,6 +126,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * context_lens       device, [num_seqs] int32
  * scale              softmax scale (1/sqrt(head_dim) on the pages); positive and finite
  * max_context_len    host bound on every context_lens[s]; at most max_blocks_per_seq * block_size
+ * num_seqs, num_q_heads  at most 65535 each (grid dimensions); num_seqs * num_kv_heads at
+ *                    most 2^31 - 1 segments, and at most 2^31 - 1 tiles of 8 tokens in all
  * workspace          device, >= pa_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                    contents need no initialisation and are scratch between calls
  *
@@ -304,6 +306,8 @@ int pa_decode_fp8_append_partitions(void* out, const void* q, const void* k_new,
  * context_lens       device, [num_seqs] int32, counting the chunk
  * query_start        device, [num_seqs + 1] int32, non-decreasing, query_start[0] = 0
  * max_query_len      host bound on every n; max_context_len: host bound on every ctx
+ * num_seqs, num_q_heads  at most 65535 each; max_query_len * (num_q_heads / num_kv_heads) at
+ *                    most 2^30 rows per sequence
  * dtype              PA_F16 (PA_F32 is not built for this call)
  * Device-side checks: a sequence with n > ctx, ctx > max_context_len or n > max_query_len
  * gets NaN rows (only rows below max_query_len are ever written); a table entry outside

@@ -2371,6 +2371,8 @@ int group_tile(int group, int dtype) {
   return group >= 5 ? 8 : group >= 3 ? 4 : group;
 }
 
+constexpr int64_t kWaveCap = static_cast<int64_t>(1) << 25;  // waves of one stream launch
+
 // Geometry shared by the size query, the stream launch and the reduce launch.
 struct Geom {
   int gt = 1;        // query heads per unit
@@ -2398,7 +2400,7 @@ Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
   int64_t w = kMaxWaves;
   const int64_t want = waves_for_partition(num_seqs, g.n_units, max_context_len, partition_size);
   if (want > w) w = want;
-  g.w_cap = static_cast<int>(w > (1 << 28) ? (1 << 28) : w);
+  g.w_cap = static_cast<int>(w > kWaveCap ? kWaveCap : w);  // one-wave groups: 2^31 work-items at most
   g.rec_rows = g.gt < group ? g.gt : group;
   g.desc_bytes = align256(static_cast<size_t>(num_seqs) * g.n_units * 2 * sizeof(int));
   g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * sizeof(float));
@@ -2449,6 +2451,7 @@ int check_decode(const DecodeCall& c, Geom* g) {
     return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of block_size %d",
                 c.partition_size, c.block_size);
   if (c.num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", c.num_seqs);
+  if (c.num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", c.num_q_heads);
   *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size,
                 c.dtype);
   // tile counts and segment indexes are 32-bit in the kernels (a tile holds at least 8
@@ -2868,6 +2871,7 @@ int pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
   if (num_q_heads % num_kv_heads != 0)
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
+  if (num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", num_q_heads);
   if (num_seqs == 0) return PA_OK;
   const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, dtype);
   if (static_cast<int64_t>(num_seqs) * g.n_units > (static_cast<int64_t>(1) << 31) - 1)
@@ -3127,6 +3131,7 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks_per_seq * block_size", max_context_len);
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
+  if (num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", num_q_heads);
   if (static_cast<int64_t>(num_kv_heads) * block_size * head_dim * 2 > (static_cast<int64_t>(1) << 32) - 1)
     return fail(PA_ERR_INVALID_ARG, "one block of one layer exceeds 4 GiB");
   const int group = num_q_heads / num_kv_heads;

@@ -100,6 +100,8 @@ def _decode(**over):
     (dict(ws=None), _lib.PA_ERR_WORKSPACE),
     (dict(wsb=16), _lib.PA_ERR_WORKSPACE),
     (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),     # not 256-byte aligned
+    (dict(S=65536), _lib.PA_ERR_INVALID_ARG),        # grid dimension limits
+    (dict(hq=65536, hkv=8), _lib.PA_ERR_INVALID_ARG),
     # more than 2^31 - 1 segments (sequence x kv head), even with empty contexts
     (dict(S=65535, hkv=40000, hq=40000, D=64, B=8, mcl=0, wsb=1 << 50), _lib.PA_ERR_INVALID_ARG),
 ])
