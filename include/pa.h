@@ -217,9 +217,9 @@ int pa_decode_append_partitions(void* out, const void* q, const void* k_new, con
  * c of the K pool means value(c) * k_scale, likewise for V.
  *
  * pa_cache_write_fp8 -- pa_cache_write for E4M3 pools: element x of k[t, h, :] (fp16)
- * is stored as the code nearest to y = x * (1/k_scale), where 1/k_scale is rounded once
- * to fp32 and y is one fp32 product; ties go to the even code, |y| beyond 448 saturates
- * to +-448 (code 0x7E / 0xFE), any NaN gives 0x7F.  Same for v with v_scale.
+ * is stored as the code nearest to the exact quotient x / k_scale; ties go to the even
+ * code, a quotient beyond 448 in magnitude saturates to +-448 (code 0x7E / 0xFE), +-0
+ * gives 0x00 / 0x80 and any NaN gives 0x7F.  Same for v with v_scale.
  * Slot handling, skips and races are those of pa_cache_write; num_tokens * num_kv_heads *
  * head_dim / 16 is at most 2^31 - 256 per call (one thread per 16 codes).
  *

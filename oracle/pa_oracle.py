@@ -469,20 +469,23 @@ def e4m3_encode(x) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(0x7F), code).astype(np.uint8)
 
 
-def fp8_inverse_scale(scale: float) -> np.float32:
-    """The single-precision reciprocal 1/scale that the store multiplies by (rounded once)."""
-    return np.float32(1.0 / float(scale))
+def fp8_quotient(x, scale: float) -> np.ndarray:
+    """x / scale in float64, with scale taken as the single-precision value the library
+    receives.  For fp16 (or fp32) x this is the exact quotient up to one float64 rounding,
+    which cannot move it across or onto a midpoint between two E4M3 values: a midpoint has
+    at most 5 significant bits, so a quotient that is not exactly on one differs from it by
+    far more than 2^-53 relative."""
+    s = np.float64(np.float32(scale))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return np.asarray(x, dtype=np.float64) / s
 
 
 def cache_write_fp8(k, v, slot_mapping, k_cache, v_cache, block_size: int, k_scale: float,
                     v_scale: float):
-    """Like cache_write, but each stored element is the E4M3 code of x / scale.
-
-    The quotient is taken the way the store takes it: x (fp16) times the
-    single-precision 1/scale, as one single-precision product.
-    """
-    kq = e4m3_encode(np.asarray(k, dtype=np.float32) * fp8_inverse_scale(k_scale))
-    vq = e4m3_encode(np.asarray(v, dtype=np.float32) * fp8_inverse_scale(v_scale))
+    """Like cache_write, but each stored element is the E4M3 code nearest to x / scale
+    (ties to the even code, saturating, NaN to 0x7F), the quotient taken exactly."""
+    kq = e4m3_encode(fp8_quotient(k, k_scale))
+    vq = e4m3_encode(fp8_quotient(v, v_scale))
     return cache_write(kq, vq, slot_mapping, k_cache, v_cache, block_size)
 
 

@@ -315,45 +315,64 @@ __global__ __launch_bounds__(256) void pa_cache_write_kernel(
   *reinterpret_cast<u32x4*>(v_cache + dst) = vx;
 }
 
-// E4M3 code of y: the nearest value (ties to an even code), saturated to +-448; any
-// NaN becomes 0x7F (its sign is not kept: the multiply before need not keep it).  Normal range: round the fp32 bit pattern
-// to 3 mantissa bits (a carry moves into the exponent) and rebase the exponent from
-// bias 127 to 7.  Below 2^-6 the codes are steps of 2^-9: round y * 2^9 to an integer.
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t bits = as_u(y);
-  const uint32_t sign = (bits >> 24) & 0x80u;
-  const uint32_t mag = bits & 0x7FFFFFFFu;
-  const float a = as_f(mag);
-  uint32_t c;
-  if (mag > 0x7F800000u) return 0x7Fu;
-  if (a >= 448.0f) {
-    c = 0x7Eu;
-  } else if (a >= 0.015625f) {
-    c = ((mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20) - (120u << 3);
-  } else {
-    c = static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
-  }
-  return c | sign;
+// An E4M3 store scale: the scale s (positive, finite) and 1/s rounded once to fp32.
+struct F8Scale {
+  float s, inv;
+};
+
+// E4M3 code nearest to the exact quotient x / s (ties to the even code), saturated to +-448;
+// +-0 stays +-0 and any NaN becomes 0x7F (its sign carries no value).  The value of the code
+// goes to `val` (every E4M3 value is exact in fp16).
+// y = x * inv lies within about 2^-22 of x / s (relative).  Rounding |y| toward zero onto
+// the E4M3 grid gives a code c0 such that |x| / s rounds to c0 or to c0 + 1 (the next value
+// up): where |y| and |x| / s fall on two sides of a code value, that value is the nearest to
+// both.  The midpoint m between the two values decides, by the sign of |x| - m s, which one
+// fma gives with a single rounding: it is zero only when |x| / s equals m (then the even
+// code), and otherwise far above the fp32 subnormal range.  Normal range: truncate the fp32
+// bit pattern to 3 mantissa bits and rebase the exponent from bias 127 to 7 (the midpoint
+// sets the fourth mantissa bit).  Below 2^-6 the codes are steps of 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code_exact(float x, F8Scale sc, float& val) {
+  const float ax = __builtin_fabsf(x);
+  const float a = __builtin_fabsf(x * sc.inv);
+  const uint32_t mag = as_u(a);
+  const bool nrm = a >= 0.015625f;
+  const float k = __builtin_fminf(__builtin_floorf(a * 512.0f), 7.0f);  // below 2^-6: 0..7; NaN: 7
+  const uint32_t c0 = nrm ? (mag >> 20) - (120u << 3) : static_cast<uint32_t>(k);
+  const float v0 = nrm ? as_f(mag & 0xFFF00000u) : k * (1.0f / 512.0f);
+  const float m = nrm ? as_f((mag & 0xFFF00000u) | 0x00080000u) : (k + 0.5f) * (1.0f / 512.0f);
+  const float r = __builtin_fmaf(-m, sc.s, ax);
+  const bool up = r > 0.0f || (r == 0.0f && (c0 & 1u) != 0u);
+  uint32_t c = up ? c0 + 1u : c0;
+  float v = up ? 2.0f * m - v0 : v0;  // the next value up, exactly
+  const bool sat = a >= 448.0f;       // infinities too
+  c = sat ? 0x7Eu : c;
+  v = sat ? 448.0f : v;
+  const bool zero = ax == 0.0f;  // also when inv overflowed to infinity (x * inv is NaN)
+  c = zero ? 0u : c;
+  v = zero ? 0.0f : v;
+  const bool nan = !(ax == ax);
+  val = nan ? __builtin_nanf("") : as_f(as_u(v) | (as_u(x) & 0x80000000u));
+  return nan ? 0x7Fu : (c | ((as_u(x) >> 24) & 0x80u));
 }
 
-// Eight fp16 values times inv, as eight E4M3 codes (byte i = element i).
-__device__ __forceinline__ u32x2 encode8(const u32x4& x, float inv) {
+// Eight fp16 values stored with scale sc, as eight E4M3 codes (byte i = element i).
+__device__ __forceinline__ u32x2 encode8(const u32x4& x, F8Scale sc) {
   uint32_t w[2] = {0u, 0u};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const f16x2 h = word_as<f16x2>(x, i / 2);
-    const float y = static_cast<float>(h[i % 2]) * inv;
-    w[i / 4] |= e4m3_code(y) << (8 * (i % 4));
+    float val;
+    w[i / 4] |= e4m3_code_exact(static_cast<float>(h[i % 2]), sc, val) << (8 * (i % 4));
   }
   return u32x2{w[0], w[1]};
 }
 
 // E4M3 pools: one thread per 16 codes (two 16-byte fp16 chunks) of one (token, kv head)
-// row.  Each element is stored as the code of x * inv_scale, one fp32 product.
+// row.  Each element is stored as the code nearest to x / scale.
 template <int D>
 __global__ __launch_bounds__(256) void pa_cache_write_fp8_kernel(
     const f16* __restrict__ k, const f16* __restrict__ v, const int64_t* __restrict__ slot_mapping,
-    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float k_inv, float v_inv,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, F8Scale ks, F8Scale vs,
     int64_t num_chunks, int num_kv_heads, int block_size, int64_t num_slots) {
   constexpr int kChunksPerRow = D / 16;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -370,8 +389,8 @@ __global__ __launch_bounds__(256) void pa_cache_write_fp8_kernel(
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * D + c * 16;
-  const u32x2 ka = encode8(k0, k_inv), kb = encode8(k1, k_inv);
-  const u32x2 va = encode8(v0, v_inv), vb = encode8(v1, v_inv);
+  const u32x2 ka = encode8(k0, ks), kb = encode8(k1, ks);
+  const u32x2 va = encode8(v0, vs), vb = encode8(v1, vs);
   *reinterpret_cast<u32x4*>(k_cache + dst) = u32x4{ka[0], ka[1], kb[0], kb[1]};
   *reinterpret_cast<u32x4*>(v_cache + dst) = u32x4{va[0], va[1], vb[0], vb[1]};
 }
@@ -420,7 +439,7 @@ struct StreamArgs {
   // ([num_seqs, num_kv_heads, head_dim]) instead of the pools
   const char* k_new;
   const char* v_new;
-  float k_inv, v_inv;  // E4M3 append mode: the reciprocal scales the new rows are coded with
+  F8Scale k_sc, v_sc;  // E4M3 append mode: the scales the new rows are coded with
 };
 
 // Append mode of the reduce kernel: where the new tokens' rows go (k_new == nullptr: off).
@@ -434,8 +453,8 @@ struct AppendArgs {
   int block_size;
   int num_kv_heads;
   int64_t num_blocks;
-  int codes;           // E4M3 pools: store code(x * inv) of each element
-  float k_inv, v_inv;  // 1/k_scale and 1/v_scale rounded to fp32
+  int codes;           // E4M3 pools: store the code nearest to x / scale of each element
+  F8Scale k_sc, v_sc;
 };
 
 // Position of a wave in the flattened tile list (all wave-uniform, in SGPRs).
@@ -1230,27 +1249,16 @@ __device__ __forceinline__ void load_entries4(const int32_t* a0, const int32_t* 
       : "memory");
 }
 
-// The value of the E4M3 code of y (e4m3_code), computed without the code and without
-// branches: round to nearest even at 3 mantissa bits in the normal range, to a multiple of
-// 2^-9 below 2^-6, 448 from 448 up, NaN for NaN.  Values of codes are exact in fp16.
-__device__ __forceinline__ float e4m3_value_of(float y) {
-  const uint32_t bits = as_u(y);
-  const uint32_t mag = bits & 0x7FFFFFFFu;
-  const float a = as_f(mag);
-  const float normal = as_f((mag + 0x7FFFFu + ((mag >> 20) & 1u)) & 0xFFF00000u);
-  const float sub = __builtin_rintf(a * 512.0f) * (1.0f / 512.0f);
-  float q = a >= 0.015625f ? normal : sub;
-  q = a >= 448.0f ? 448.0f : q;
-  return as_f(as_u(q) | (bits & 0x80000000u));
-}
-
-// Eight fp16 values times inv, each replaced by the fp16 value of its E4M3 code.
-__device__ __forceinline__ f16x8 e4m3_values8(const u32x4& x, float inv) {
+// Eight fp16 values, each replaced by the fp16 value of the E4M3 code the store gives it
+// with scale sc.
+__device__ __forceinline__ f16x8 e4m3_values8(const u32x4& x, F8Scale sc) {
   f16x8 r;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const f16x2 h = word_as<f16x2>(x, i / 2);
-    r[i] = static_cast<f16>(e4m3_value_of(static_cast<float>(h[i % 2]) * inv));
+    float val;
+    (void)e4m3_code_exact(static_cast<float>(h[i % 2]), sc, val);
+    r[i] = static_cast<f16>(val);
   }
   return r;
 }
@@ -1701,12 +1709,12 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
         if (g == tn) {
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
-            kop[kb] = e4m3_values8(nkr[kb], a.k_inv);
+            kop[kb] = e4m3_values8(nkr[kb], a.k_sc);
           }
         }
         if (jq == (tn >> 2)) {
           const int t = tn & 3;
-          const f16x8 qv = e4m3_values8(nvr, a.v_inv);
+          const f16x8 qv = e4m3_values8(nvr, a.v_sc);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
             const f16 val = qv[nb];
@@ -2300,9 +2308,9 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
           const int c = lane % kC;
           const bool isv = lane >= kC;
           const char* src = (isv ? ap.v_new : ap.k_new) + row * (2 * D) + c * 32;
-          const float inv = isv ? ap.v_inv : ap.k_inv;
-          const u32x2 lo = encode8(*reinterpret_cast<const u32x4*>(src), inv);
-          const u32x2 hi = encode8(*reinterpret_cast<const u32x4*>(src + 16), inv);
+          const F8Scale sc = isv ? ap.v_sc : ap.k_sc;
+          const u32x2 lo = encode8(*reinterpret_cast<const u32x4*>(src), sc);
+          const u32x2 hi = encode8(*reinterpret_cast<const u32x4*>(src + 16), sc);
           *reinterpret_cast<u32x4*>((isv ? ap.v_cache : ap.k_cache) + slot * D + c * 16) =
               u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
@@ -2339,8 +2347,9 @@ using pa_detail::g_error;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
-// E4M3 stores multiply by the reciprocal scale, rounded once to fp32
-float inv_scale(float scale) { return static_cast<float>(1.0 / static_cast<double>(scale)); }
+// An E4M3 store scale and its reciprocal, rounded once to fp32 (the kernels use it to find
+// the two codes nearest to x / scale, and the scale itself to choose between them exactly)
+F8Scale f8_scale(float scale) { return F8Scale{scale, static_cast<float>(1.0 / static_cast<double>(scale))}; }
 
 int log2_of(int x) {
   int l = 0;
@@ -2621,8 +2630,8 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   }
   a.k_new = static_cast<const char*>(c.k_new);
   a.v_new = static_cast<const char*>(c.v_new);
-  a.k_inv = inv_scale(c.k_scale);
-  a.v_inv = inv_scale(c.v_scale);
+  a.k_sc = f8_scale(c.k_scale);
+  a.v_sc = f8_scale(c.v_scale);
   return a;
 }
 
@@ -2661,8 +2670,8 @@ int launch_reduce(const DecodeCall& c, const Geom& g) {
     ap.num_kv_heads = c.num_kv_heads;
     ap.num_blocks = c.num_blocks;
     ap.codes = c.kv_fp8 ? 1 : 0;
-    ap.k_inv = inv_scale(c.k_scale);
-    ap.v_inv = inv_scale(c.v_scale);
+    ap.k_sc = f8_scale(c.k_scale);
+    ap.v_sc = f8_scale(c.v_scale);
   }
   hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
                      c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
@@ -2724,7 +2733,7 @@ int launch_cache_write(const void* k, const void* v, const int64_t* slots, void*
 
 template <int D>
 int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, void* kc, void* vc,
-                           float k_inv, float v_inv, int num_tokens, int num_kv_heads, int block_size,
+                           F8Scale ks, F8Scale vs, int num_tokens, int num_kv_heads, int block_size,
                            int64_t num_blocks, hipStream_t stream) {
   const int64_t chunks = static_cast<int64_t>(num_tokens) * num_kv_heads * (D / 16);
   if (chunks > kMaxWriteThreads)
@@ -2733,7 +2742,7 @@ int launch_cache_write_fp8(const void* k, const void* v, const int64_t* slots, v
   const int64_t blocks = (chunks + 255) / 256;
   hipLaunchKernelGGL((pa_cache_write_fp8_kernel<D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                      stream, static_cast<const f16*>(k), static_cast<const f16*>(v), slots,
-                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), k_inv, v_inv, chunks,
+                     static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), ks, vs, chunks,
                      num_kv_heads, block_size, num_blocks * block_size);
   return check_hip("pa_cache_write_fp8_kernel launch");
 }
@@ -2980,14 +2989,13 @@ int pa_cache_write_fp8(const void* k, const void* v, const int64_t* slot_mapping
   if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return fail(PA_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(slot_mapping, 8)) return fail(PA_ERR_INVALID_ARG, "slot_mapping must be 8-byte aligned");
-  // the reciprocal is rounded once, to fp32; every element is then one fp32 product
-  const float k_inv = inv_scale(k_scale);
-  const float v_inv = inv_scale(v_scale);
+  const F8Scale k_sc = f8_scale(k_scale);
+  const F8Scale v_sc = f8_scale(v_scale);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return head_dim == 64
-             ? launch_cache_write_fp8<64>(k, v, slot_mapping, k_cache, v_cache, k_inv, v_inv, num_tokens,
+             ? launch_cache_write_fp8<64>(k, v, slot_mapping, k_cache, v_cache, k_sc, v_sc, num_tokens,
                                           num_kv_heads, block_size, num_blocks, st)
-             : launch_cache_write_fp8<128>(k, v, slot_mapping, k_cache, v_cache, k_inv, v_inv, num_tokens,
+             : launch_cache_write_fp8<128>(k, v, slot_mapping, k_cache, v_cache, k_sc, v_sc, num_tokens,
                                            num_kv_heads, block_size, num_blocks, st);
 }
 

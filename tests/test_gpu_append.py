@@ -271,3 +271,29 @@ def test_fp8_split_launches_and_nothing_stored_for_bad_sequences():
     assert torch_equal(kc, ek) and torch_equal(vc, ev)
     ref, _, _ = _f8_two_calls(case, d, ks, vs, 0)
     assert got[[0, 4, 5, 6]].tobytes() == ref[[0, 4, 5, 6]].tobytes()
+
+
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 8)])
+def test_fp8_append_rounds_near_midpoint_quotients_exactly(D, B):
+    """New rows made of fp16 values whose quotient by the scale lies within an fp32 step of a
+    midpoint between two codes: the reduce kernel's store and the operands the attention kernel
+    substitutes for the new token must both take the code nearest to the exact quotient."""
+    F = _f8()
+    ks, vs = F._near_midpoint_scales(3)[1:3]
+    case = W.make_case(seed=5 + D, dtype=np.float16, context_lens=[1, 17, 40, 100], num_q_heads=8,
+                       num_kv_heads=2, head_dim=D, block_size=B, sigma=0.5)
+    rng = np.random.default_rng(D)
+    for arr, sc in ((case.new_k, ks), (case.new_v, vs)):
+        hard = F._ALL_F16[(F._reciprocal_reading(sc) != F._codes(F._ALL_F16, sc)) & np.isfinite(F._ALL_F16)]
+        assert hard.size > 0
+        arr[...] = rng.choice(hard, size=arr.shape)
+    G.say(f"fp8 append near-midpoint D{D} B{B} scales {ks!r} {vs!r}")
+    d = _f8_device(case, ks, vs)
+    got, kc, vc = _f8_append(case, d, ks, vs, 0)
+    ref, rkc, rvc = _f8_two_calls(case, d, ks, vs, 0)
+    assert got.tobytes() == ref.tobytes(), "output differs from write + decode"
+    assert torch_equal(kc, rkc) and torch_equal(vc, rvc), "pools differ from write + decode"
+    okc, ovc = F._oracle_pools(case, ks, vs)
+    assert kc.cpu().numpy().tobytes() == okc.tobytes(), "K codes differ from the oracle's"
+    assert vc.cpu().numpy().tobytes() == ovc.tobytes(), "V codes differ from the oracle's"
+    F._check(got, F._oracle_decode(case, okc, ovc, ks, vs), ovc, vs, "near-midpoint append")

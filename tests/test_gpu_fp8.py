@@ -46,7 +46,7 @@ def _codes(x, scale):
     """The oracle's E4M3 store of fp16 x.  The store is elementwise, so it is evaluated once
     per fp16 bit pattern and looked up (cache_write_fp8 itself is checked on every pattern)."""
     with np.errstate(invalid="ignore"):  # NaN patterns stay NaN
-        lut = O.e4m3_encode(_ALL_F16.astype(np.float32) * O.fp8_inverse_scale(scale))
+        lut = O.e4m3_encode(O.fp8_quotient(_ALL_F16, scale))
     return lut[np.ascontiguousarray(x, dtype=np.float16).view(np.uint16)]
 
 
@@ -105,14 +105,43 @@ def _check(got, ref, vc, vs, label):
     assert np.all(err <= bound), f"{label}: {err[worst]:.3e} > {bound[worst]:.3e} at {worst}"
 
 
+def _reciprocal_reading(scale):
+    """Codes of every fp16 value under the fp32-product reading x * fp32(1/scale) (not the
+    store's definition): used only to show that a scale puts some quotient near a midpoint."""
+    with np.errstate(all="ignore"):
+        return O.e4m3_encode(_ALL_F16.astype(np.float32) * np.float32(1.0 / scale))
+
+
+def _near_midpoint_scales(n=4, seed=21):
+    """fp32 scales for which some fp16 x has x / scale within an fp32 step of a midpoint
+    between two E4M3 values, so that a product with a rounded reciprocal would round it the
+    wrong way: the scale of the worked counterexample (3.873046875 / scale just below 76), and
+    scales fp32(x / m) +- one step for seeded x and midpoints m."""
+    pos = O.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    fin = _ALL_F16[np.isfinite(_ALL_F16) & (_ALL_F16 > 0)].astype(np.float64)
+    rng = np.random.default_rng(seed)
+    out = [0.050961144268512726]
+    while len(out) < n:
+        s0 = np.float32(float(rng.choice(fin)) / float(rng.choice(mids)))
+        for t in (np.nextafter(s0, np.float32(0), dtype=np.float32), s0,
+                  np.nextafter(s0, np.float32(np.inf), dtype=np.float32)):
+            if len(out) < n and 1e-6 < t < 1e6 and not np.array_equal(_reciprocal_reading(float(t)),
+                                                                          _codes(_ALL_F16, float(t))):
+                out.append(float(t))
+    return out
+
+
 # ------------------------------------------------------------------ the store
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("scale", [1.0, 0.037, 3.0, 2.0 ** -7, 1e-3])
+@pytest.mark.parametrize("scale", [1.0, 0.037, 3.0, 2.0 ** -7, 1e-3] + _near_midpoint_scales())
 def test_store_every_fp16_value_bit_exact(D, scale):
     """All 65536 fp16 bit patterns (NaN, infinities, subnormals, both zeros) through the
-    store at several scales, slots shuffled over a larger pool: byte-equal to the oracle."""
+    store at several scales, slots shuffled over a larger pool: byte-equal to the oracle.  The
+    near-midpoint scales put some quotients within an fp32 step of a midpoint between two
+    codes, where only the exact quotient rounds the right way."""
     torch = _torch()
-    G.say(f"fp8 store D{D} scale {scale}")
+    G.say(f"fp8 store D{D} scale {scale!r}")
     hkv, B = 4, 16
     pats = np.arange(65536, dtype=np.uint16).view(np.float16)
     T = 65536 // (hkv * D)

@@ -8,6 +8,7 @@ format's definition and to torch's own float8_e4m3fn conversion, and tie the FP8
 to the already pinned fp64 definition.
 """
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -87,23 +88,72 @@ def test_f5_saturation_and_brute_force_nearest():
     assert np.array_equal(np.abs(np.clip(x, -448, 448) - got), best)
 
 
-def test_f6_store_is_the_single_precision_quotient():
-    """The stored code of x is that of fp32(x) * fp32(1/scale), one rounding each."""
-    case = W.make_case(seed=5, dtype=np.float16, context_lens=[3, 20], num_q_heads=4,
-                       num_kv_heads=2, head_dim=16, block_size=8, sigma=2.0)
-    pool = np.zeros((case.num_blocks, case.num_kv_heads, case.block_size, case.head_dim), np.uint8)
-    ks, vs = 0.037, 3.0
-    kc, vc = O.cache_write_fp8(case.prefix_k, case.prefix_v, case.prefix_slots, pool, pool,
-                               case.block_size, ks, vs)
-    inv = np.float32(1.0) / np.float64(ks)  # the same reciprocal, taken another way
-    assert O.fp8_inverse_scale(ks) == np.float32(inv)
-    slot = int(case.prefix_slots[7])
-    blk, off = slot // case.block_size, slot % case.block_size
-    x = case.prefix_k[7].astype(np.float32) * np.float32(inv)
-    assert np.array_equal(kc[blk, :, off, :], O.e4m3_encode(x))
-    # dequantized error is at most half a code step relative (2^-4) plus the subnormal step
-    deq = O.dequantize_pool(kc[blk, :, off, :], ks)
-    ref = case.prefix_k[7].astype(np.float64)
+def _exact_code(x: float, scale: float) -> int:
+    """Nearest E4M3 code to x / scale in exact rational arithmetic (pure Python): every
+    finite non-negative value is compared with |x| / scale (clamped to 448), ties to the even
+    code, the sign of x added.  Independent of the oracle's float64 quotient."""
+    if math.isnan(x):
+        return 0x7F
+    q = min(abs(Fraction(x) / Fraction(scale)), Fraction(448))
+    best = None
+    for c in range(0x7F):
+        d = abs(q - Fraction(O.e4m3_value(c)))
+        if best is None or d < best[0] or (d == best[0] and c % 2 == 0):
+            best = (d, c)
+    return best[1] | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+
+def _near_midpoint_pairs(n, seed):
+    """(x, scale) pairs whose exact quotient lies within a few fp32 steps of a midpoint between
+    two E4M3 values: scale = fp32(x / m) and its fp32 neighbours."""
+    rng = np.random.default_rng(seed)
+    pos = O.E4M3_TABLE[:0x7F]
+    mids = (pos[:-1] + pos[1:]) / 2.0
+    f16 = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
+    f16 = f16[np.isfinite(f16) & (f16 != 0)]
+    pairs = []
+    while len(pairs) < n:
+        x, m = float(rng.choice(f16)), float(rng.choice(mids))
+        s = np.float32(abs(x) / m)
+        if not (np.isfinite(s) and s > 0):
+            continue
+        for step in (-1, 0, 1):
+            t = s if step == 0 else np.nextafter(s, np.float32(np.inf if step > 0 else 0.0), dtype=np.float32)
+            pairs.append((x, float(t)))
+    return pairs
+
+
+def test_f6_store_is_the_nearest_code_to_the_exact_quotient():
+    """The stored code of x is the code nearest to x / scale itself.  x = 3.873046875 with the
+    fp32 scale 0.050961144268512726 has x / scale = 75.99999825, just below the midpoint 76
+    between 72 and 80, so the code is 0x69 (72); the fp32 product x * fp32(1/scale) rounds to
+    76.0 exactly and would give the even code 0x6A (80)."""
+    x, s = 3.873046875, 0.050961144268512726
+    assert float(np.float16(x)) == x and float(np.float32(s)) == s
+    assert Fraction(x) / Fraction(s) < 76 and O.e4m3_value(0x69) == 72.0
+    assert _exact_code(x, s) == 0x69
+    pool = np.zeros((1, 1, 1, 1), np.uint8)
+    k = np.array([[[x]]], np.float16)
+    kc, vc = O.cache_write_fp8(k, -k, np.array([0], np.int64), pool, pool, 1, s, s)
+    assert kc[0, 0, 0, 0] == 0x69 and vc[0, 0, 0, 0] == 0xE9
+    # near-midpoint pairs, exact ties among them, and random pairs: exact rational arithmetic
+    rng = np.random.default_rng(11)
+    pairs = _near_midpoint_pairs(300, 6)
+    pairs += [(float(np.float16(v)), float(np.float32(sc))) for v, sc in
+              zip(rng.standard_normal(200) * 4, np.exp(rng.uniform(-8, 3, 200)))]
+    pairs += [(72.0 * 0.25 + 8.0 * 0.125, 0.25), (3.0, 2.0 ** -5 / 1.0), (-0.0, 1.0), (0.0, 3.0)]
+    xs = np.array([p[0] for p in pairs], np.float16)
+    ss = [p[1] for p in pairs]
+    got = [int(O.e4m3_encode(O.fp8_quotient(xs[i:i + 1], ss[i]))[0]) for i in range(len(pairs))]
+    want = [_exact_code(float(xs[i]), ss[i]) for i in range(len(pairs))]
+    assert got == want
+    # in range, the dequantized error is at most half a code step relative (2^-4) plus half
+    # the subnormal step
+    ks = 0.037
+    ref = xs.astype(np.float64)
+    ref = ref[np.abs(ref) <= 448.0 * ks]
+    deq = O.dequantize_pool(O.e4m3_encode(O.fp8_quotient(ref, ks)), ks)
+    assert ref.size > 100
     assert np.all(np.abs(deq - ref) <= 2.0 ** -4 * np.abs(ref) + 2.0 ** -10 * ks + 1e-12)
 
 
@@ -131,6 +181,17 @@ def test_f7_fp8_decode_is_attention_on_the_dequantized_pools():
     want = O.decode(case.q, kc, vc, case.block_tables, case.context_lens, case.scale,
                     case.block_size, case.num_kv_heads)
     assert np.array_equal(got, want)
+
+
+def test_f8_planted_reciprocal_quotient_is_caught(monkeypatch):
+    """Storing the code of the fp32 product x * fp32(1/scale) instead of x / scale fails F6."""
+    def recip(x, scale):
+        with np.errstate(all="ignore"):
+            return np.asarray(x, np.float32) * np.float32(1.0 / float(scale))
+
+    monkeypatch.setattr(O, "fp8_quotient", recip)
+    with pytest.raises(AssertionError):
+        test_f6_store_is_the_nearest_code_to_the_exact_quotient()
 
 
 @pytest.mark.parametrize("mutant", ["ties_up", "no_saturation", "lost_sign"])
