@@ -76,8 +76,8 @@ def _fp16_bound(got, ref, case, label):
 # ------------------------------------------------------------------ the five workloads
 @functools.lru_cache(maxsize=1)
 def _config(name, variant):
-    if name == "long_context_b16":
-        return W.long_context(16, variant)
+    if name.startswith("long_context_b"):  # the block-size sweep: B = 8, 16, 32
+        return W.long_context(int(name[len("long_context_b"):]), variant)
     return W.CONFIGS[name](variant)
 
 
@@ -88,6 +88,8 @@ CONFIG_RUNS = [
     ("shared_prefix", "plain", 0), ("shared_prefix", "needle", 512),
     ("shared_prefix", "poscode", 0),
     ("long_context_b16", "plain", 0), ("long_context_b16", "needle", 512),
+    ("long_context_b8", "plain", 0), ("long_context_b8", "needle", 512),
+    ("long_context_b32", "plain", 0), ("long_context_b32", "needle", 512),
 ]
 
 
