@@ -3,7 +3,8 @@
  *
  * C ABI of libpa.so.  Plain pointers and sizes only; every tensor argument is
  * device memory owned by the caller.  The library allocates nothing, keeps no
- * state besides the thread-local error string, never synchronises, and puts
+ * state besides the thread-local error string (and the static scratch array of
+ * pa_decode_noalloc, one per GPU), never synchronises, and puts
  * every kernel on the stream it is given (a hipStream_t passed as void*;
  * NULL is the default stream).  Calls are asynchronous: a fault inside a
  * kernel surfaces as a HIP error at the caller's next synchronisation.
@@ -144,6 +145,27 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
               int32_t partition_size, int32_t dtype,
               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments
+ * as pa_decode without the workspace; same kernels, work split and results, bit for bit.
+ * Its scratch (the segment descriptors and piece records a workspace would hold) is a
+ * static device array of PA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; the call itself allocates nothing.  Sizes whose scratch
+ * would exceed that (records for every persistent wave of the launch: at the default split
+ * this covers every head_dim and group size) return PA_ERR_WORKSPACE with nothing launched.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on two
+ * streams, or from two threads) race and must be serialised by the caller.  The array needs
+ * no clearing: whatever a call reads of it, the same call wrote first.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens,
+                      float scale, int32_t block_size, int32_t num_kv_heads,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                      int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                      int32_t partition_size, int32_t dtype, void* stream);
 
 /*
  * pa_decode_partitions / pa_decode_reduce -- the two launches pa_decode makes,
@@ -433,7 +455,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 6)
+#define PA_ABI_VERSION ((2 << 16) | 7)
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ from ._lib import (  # noqa: F401
     pa_decode_fp8_append,
     pa_decode_fp8_append_partitions,
     pa_decode_fp8_partitions,
+    pa_decode_noalloc,
     pa_decode_partitions,
     pa_decode_reduce,
     pa_decode_workspace_bytes,

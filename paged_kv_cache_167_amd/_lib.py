@@ -39,6 +39,9 @@ SIGNATURES = {
     "pa_decode": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
                              _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64, _c_int32,
                              _c_int32, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_noalloc": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
+                                     _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64,
+                                     _c_int32, _c_int32, _vp]),
     "pa_decode_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32,
                                         _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                         _c_int64, _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
@@ -206,6 +209,22 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
                                    workspace, stream)
     _check("pa_decode", lib().pa_decode(*args))
     return workspace
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                      num_kv_heads, max_context_len=None, partition_size=DEFAULT_PARTITION,
+                      stream=None) -> None:
+    """pa_decode with no workspace: the library's static scratch serves as one, and nothing
+    is allocated (neither here nor in the library)."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    code = lib().pa_decode_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+        float(scale), int(block_size), int(num_kv_heads), num_seqs, num_q_heads, head_dim, max_blocks,
+        int(max_context_len), k_cache.shape[0], int(partition_size), _dtype_code(q), _stream(q, stream))
+    _check("pa_decode_noalloc", code)
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,

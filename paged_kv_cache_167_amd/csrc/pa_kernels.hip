@@ -2418,6 +2418,16 @@ Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
   return g;
 }
 
+// The same layout with records for exactly `waves` waves (at most g.w_cap): the smallest
+// scratch one launch of that many waves needs.
+Geom with_waves(Geom g, int waves, int head_dim) {
+  g.w_cap = waves;
+  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * sizeof(float));
+  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * head_dim * sizeof(float));
+  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
+  return g;
+}
+
 struct DecodeCall {
   void* out;
   const void* q;
@@ -2440,7 +2450,8 @@ struct DecodeCall {
   const void* v_new = nullptr;
 };
 
-int check_decode(const DecodeCall& c, Geom* g) {
+// need_ws false: every check but the workspace's (the caller brings its own scratch)
+int check_decode(const DecodeCall& c, Geom* g, bool need_ws = true) {
   int rc = check_common(c.dtype, c.head_dim, c.block_size);
   if (rc != PA_OK) return rc;
   if (!(c.scale > 0.0f) || !std::isfinite(c.scale))
@@ -2481,10 +2492,12 @@ int check_decode(const DecodeCall& c, Geom* g) {
     return fail(PA_ERR_INVALID_ARG, "out, q, k_cache and v_cache must be 16-byte aligned");
   if (!aligned(c.block_tables, 4) || !aligned(c.context_lens, 4))
     return fail(PA_ERR_INVALID_ARG, "block_tables and context_lens must be 4-byte aligned");
-  if (!c.workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g->ws_bytes);
-  if (c.workspace_bytes < g->ws_bytes)
-    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.workspace_bytes, g->ws_bytes);
-  if (!aligned(c.workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (need_ws) {
+    if (!c.workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g->ws_bytes);
+    if (c.workspace_bytes < g->ws_bytes)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", c.workspace_bytes, g->ws_bytes);
+    if (!aligned(c.workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
   if (c.k_new || c.v_new) {
     if (!c.k_new || !c.v_new) return fail(PA_ERR_INVALID_ARG, "k_new or v_new is NULL");
     if (!aligned(c.k_new, 16) || !aligned(c.v_new, 16))
@@ -2774,6 +2787,51 @@ int launch_prefill(const PrefillArgs& a, int64_t rows, int num_seqs, hipStream_t
   return launch_prefill_rows<D, kPfBlocks>(a, rows, num_seqs, stream);
 }
 
+// Waves of pa_decode's stream launch for these sizes on the current device (0 if the
+// occupancy query fails): the split the launch itself will pick.
+template <int D>
+int decode_waves(const DecodeCall& c, const Geom& g) {
+  if (c.dtype == PA_F16) return waves_mfma<D, kMfStages, false, false, false>(c, g, kMfWavesPerCU);
+  switch (g.gt) {
+    case 1: return waves_valu<float, D, 1>(c, g);
+    case 2: return waves_valu<float, D, 2>(c, g);
+    case 4: return waves_valu<float, D, 4>(c, g);
+    default: return waves_valu<float, D, 8>(c, g);
+  }
+}
+
+// Scratch of pa_decode_noalloc: segment descriptors and piece records, laid out as a
+// workspace.  One copy per GPU, held until the process ends; no call needs it cleared (every
+// descriptor and record a call reads, the same call wrote first).
+constexpr size_t kScratchBytes = static_cast<size_t>(PA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per device with that
+// device current (each GPU holds its own copy at its own address).  In host code the name
+// `scratch` is only a stand-in: kernels and copies must be given this address.
+int scratch_address(void** out) {
+  constexpr int kDevs = 64;
+  static std::mutex mu;
+  static void* addr[kDevs] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) {
+    (void)hipGetLastError();
+    return fail(PA_ERR_HIP, "no current device (or device index %d above %d)", dev, kDevs - 1);
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(PA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    }
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return PA_OK;
+}
+
 DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* v_cache,
                      const int32_t* block_tables, const int32_t* context_lens, float scale,
                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
@@ -2924,6 +2982,34 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   rc = dispatch<0>(c, g);
   if (rc != PA_OK) return rc;
   return dispatch<1>(c, g);
+}
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                      int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int64_t num_blocks, int32_t partition_size, int32_t dtype, void* stream) {
+  g_error.clear();
+  DecodeCall c = make_call(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                           num_kv_heads, num_seqs, num_q_heads, head_dim, max_blocks_per_seq,
+                           max_context_len, num_blocks, partition_size, dtype, nullptr, 0, stream);
+  Geom g;
+  int rc = check_decode(c, &g, false);
+  if (rc != PA_OK || c.num_seqs == 0) return rc;
+  const int waves = head_dim == 64 ? decode_waves<64>(c, g) : decode_waves<128>(c, g);
+  if (waves <= 0) return fail(PA_ERR_HIP, "occupancy query for the decode kernel failed");
+  const Geom gs = with_waves(g, waves, head_dim);
+  if (gs.ws_bytes > kScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "these sizes need %zu bytes of scratch, above the %zu this call holds; use pa_decode "
+                "with a workspace",
+                gs.ws_bytes, kScratchBytes);
+  rc = scratch_address(&c.workspace);
+  if (rc != PA_OK) return rc;
+  c.workspace_bytes = kScratchBytes;
+  rc = dispatch<0>(c, gs);
+  if (rc != PA_OK) return rc;
+  return dispatch<1>(c, gs);
 }
 
 static int decode_append(int launches, void* out, const void* q, const void* k_new, const void* v_new,

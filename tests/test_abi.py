@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 6
+    assert P.lib().pa_abi_version() == (2 << 16) | 7
 
 
 def test_workspace_size_query():
@@ -112,6 +112,36 @@ def test_decode_rejects_bad_arguments(over, code):
 
 def test_decode_with_no_sequences_is_a_no_op():
     assert _decode(S=0, out=None, q=None) == _lib.PA_OK
+    assert P.last_error() == ""
+
+
+def _noalloc(**over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, scale=1.0, B=16, hkv=8, S=4,
+             hq=32, D=128, mb=16, mcl=256, N=100, P=64, dt=_lib.PA_F16, stream=None)
+    a.update(over)
+    return P.lib().pa_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["scale"],
+                                     a["B"], a["hkv"], a["S"], a["hq"], a["D"], a["mb"], a["mcl"], a["N"],
+                                     a["P"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(dt=7), _lib.PA_ERR_UNSUPPORTED),
+    (dict(hq=30), _lib.PA_ERR_INVALID_ARG),
+    (dict(P=24), _lib.PA_ERR_INVALID_ARG),
+    (dict(mcl=257), _lib.PA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), _lib.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(S=65536), _lib.PA_ERR_INVALID_ARG),
+])
+def test_decode_noalloc_rejects_bad_arguments(over, code):
+    """Checked on the host before the scratch or the device is touched."""
+    assert _noalloc(**over) == code
+    assert P.last_error() != ""
+
+
+def test_decode_noalloc_with_no_sequences_is_a_no_op():
+    assert _noalloc(S=0, out=None, q=None) == _lib.PA_OK
     assert P.last_error() == ""
 
 
