@@ -11,6 +11,12 @@ Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
 heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
 blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.
 
+`value` is the step rate over --steps back-to-back steps.  Each call (the dominant stream
+kernel alone, the whole decode call, the cache write) is also timed launch by launch after
+a 1 GiB read that leaves no cache holding the pool: the median of those cold launches is
+the primary per-call figure (min and mean beside it), the back-to-back average is the
+warm one.  The CPU baseline is the oracle's decode on every host core of the process.
+
 Prints one JSON line on stdout; progress goes to stderr.
 """
 
@@ -56,8 +62,10 @@ def parse():
     ap.add_argument("--partition", type=int, default=0,
                     help="partition size in tokens (0: one wave per resident slot; >0: more "
                          "waves, each taking at most about that many tokens)")
-    ap.add_argument("--cold-iters", type=int, default=10,
-                    help="extra stream-kernel launches each after a 1 GiB cache flush")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="launches of each timed call (the stream kernel, pa_decode, pa_cache_write), "
+                         "each after reading 1 GiB so that no cache holds the pool; their median "
+                         "is the primary figure")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: replay one captured HIP graph of the step instead of "
@@ -143,48 +151,55 @@ def fp8_scales(case):
     return f(case.prefix_k, case.new_k), f(case.prefix_v, case.new_v)
 
 
+def host_cores():
+    """Host cores this process may run on (its affinity mask), read at run time."""
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(case, fp8=False):
-    """The oracle, as it stands, on the same workload: write the new tokens, then decode."""
+    """The oracle, as it stands, on the same workload: its decode (the pools, new tokens
+    included, are prepared outside the timed region), on every host core of this process."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle import pa_oracle as O
-    log("cpu baseline: building the oracle's pools (not timed)")
+    cores = host_cores()
+    log(f"cpu baseline: building the oracle's pools (not timed); {cores} host cores")
     if fp8:
         ks, vs = fp8_scales(case)
         empty = np.full(case.empty_pool().shape, 0x7F, dtype=np.uint8)
         kc, vc = O.cache_write_fp8(case.prefix_k, case.prefix_v, case.prefix_slots, empty,
                                    empty.copy(), case.block_size, ks, vs)
+        kc, vc = O.cache_write_fp8(case.new_k, case.new_v, case.new_slots, kc, vc, case.block_size,
+                                   ks, vs)
     else:
         kc, vc = O.cache_write(case.prefix_k, case.prefix_v, case.prefix_slots, case.empty_pool(),
                                case.empty_pool(), case.block_size)
+        kc, vc = O.cache_write(case.new_k, case.new_v, case.new_slots, kc, vc, case.block_size)
     elt = 1 if fp8 else case.elt_bytes
     kv_all = int(case.context_lens.astype("int64").sum()) * case.num_kv_heads * case.head_dim * 2
     n = case.num_seqs
     if kv_all * case.elt_bytes > 1.5e9:  # keep the CPU leg to tens of seconds: a prefix of the batch
         n = max(1, int(n * 1.5e9 / (kv_all * case.elt_bytes)))
     reps = 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         while reps == 0 or time.perf_counter() - t0 < 10.0:  # about 10 s of CPU work
             if fp8:
-                kc2, vc2 = O.cache_write_fp8(case.new_k[:n], case.new_v[:n], case.new_slots[:n],
-                                             kc, vc, case.block_size, ks, vs)
-                O.decode_fp8(case.q[:n], kc2, vc2, ks, vs, case.block_tables[:n],
-                             case.context_lens[:n], case.scale, case.block_size, case.num_kv_heads)
+                O.decode_fp8(case.q[:n], kc, vc, ks, vs, case.block_tables[:n], case.context_lens[:n],
+                             case.scale, case.block_size, case.num_kv_heads)
             else:
-                kc2, vc2 = O.cache_write(case.new_k[:n], case.new_v[:n], case.new_slots[:n], kc,
-                                         vc, case.block_size)
-                O.decode(case.q[:n], kc2, vc2, case.block_tables[:n], case.context_lens[:n],
-                         case.scale, case.block_size, case.num_kv_heads)
+                O.decode(case.q[:n], kc, vc, case.block_tables[:n], case.context_lens[:n], case.scale,
+                         case.block_size, case.num_kv_heads)
             reps += 1
         dt = (time.perf_counter() - t0) / reps
     kv = int(case.context_lens[:n].astype("int64").sum()) * case.num_kv_heads * case.head_dim * \
         2 * elt
-    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "seconds_per_step": dt, "steps": reps, "seqs_per_s": n / dt,
-            "sample": f"{n} of {case.num_seqs} sequences, {reps} steps (write new tokens + "
-                      "decode) of about 10 s in total, numpy float64, BLAS limited to 1 thread"}
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "seconds_per_call": dt, "calls": reps, "seqs_per_s": n / dt,
+            "sample": f"{n} of {case.num_seqs} sequences, {reps} decode calls of about 10 s in total "
+                      f"(pools with the new tokens built beforehand, untimed), numpy float64, BLAS on "
+                      f"{cores} threads (the process's host cores)"}
 
 
 def main():
@@ -361,56 +376,70 @@ def run_one(args, config):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    # the dominant kernel alone: the same number of back-to-back launches between two HIP
-    # events on the launch stream; their average is its launch duration
+    # Each call is timed two ways, both with HIP events on the launch stream:
+    #  * cold (primary): one launch between two events, after reading 1 GiB so that neither L2
+    #    nor the 256 MB MALL holds the pool (a read, not a write: a writing flush would leave
+    #    dirty lines whose write-back competes with the timed kernel); median and min over
+    #    --cold-iters launches;
+    #  * warm: --steps back-to-back launches between two events, averaged.
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    stream_kernel()
-    e0.record(stream)
-    for _ in range(args.steps):
-        stream_kernel()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kern_ms_avg = e0.elapsed_time(e1) / args.steps
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev) if args.cold_iters > 0 else None
 
-    # pa_decode (both launches) and pa_cache_write, each the same way
-    per_call_ms = {}
-    for key, fn in (("decode", decode_only), ("write", write_only)):
+    def warm_ms(fn):
         fn()
         e0.record(stream)
         for _ in range(args.steps):
             fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        per_call_ms[key] = e0.elapsed_time(e1) / args.steps
-    step()  # leave the rows pa_decode writes in out
-    torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
 
-    # cold-cache launches of the same kernel: reading 1 GiB first leaves L2 and the 256 MB
-    # MALL holding clean lines of other data (a write would leave dirty lines whose
-    # write-back then competes with the kernel's reads); one launch between two events
-    cold_ms = []
-    if args.cold_iters > 0:
-        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    def cold_ms(fn):
+        times = []
         for _ in range(args.cold_iters):
             flush.sum()
             e0.record(stream)
-            stream_kernel()
+            fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            cold_ms.append(e0.elapsed_time(e1))
-        del flush
+            times.append(e0.elapsed_time(e1))
+        return times
+
+    timing = {}
+    for key, fn in (("kernel", stream_kernel), ("decode", decode_only), ("write", write_only)):
+        timing[key] = {"warm": warm_ms(fn), "cold": cold_ms(fn) if flush is not None else []}
+    del flush
+    step()  # leave the rows pa_decode writes in out
+    torch.cuda.synchronize()
+
+    def primary_ms(key):  # cold median, or the warm average when no cold launch was asked for
+        c = timing[key]["cold"]
+        return float(np.median(c)) if c else timing[key]["warm"]
+
+    def summary(key):
+        c = timing[key]["cold"]
+        d = {"warm_us": round(timing[key]["warm"] * 1e3, 2)}
+        if c:
+            d.update({"cold_median_us": round(float(np.median(c)) * 1e3, 2),
+                      "cold_min_us": round(float(np.min(c)) * 1e3, 2),
+                      "cold_mean_us": round(float(np.mean(c)) * 1e3, 2), "cold_launches": len(c)})
+        return d
 
     tokens_blocks = int(sum(-(-int(c) // case.block_size) for c in case.context_lens))
     q_bytes = case.num_seqs * case.num_q_heads * case.head_dim * case.elt_bytes
     # K/V rows, q in, out, the table entries in use and the context lengths
     alg_bytes = kv_bytes + 2 * q_bytes + tokens_blocks * 4 + case.num_seqs * 4
-    achieved = alg_bytes / (kern_ms_avg * 1e-3) / 1e9
+    kern_ms = primary_ms("kernel")
+    achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
+    warm_achieved = alg_bytes / (timing["kernel"]["warm"] * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     kernel = stream_kernel_name(case.dtype == np.float16)
     traffic = measured_traffic(kernel, config, partition)
     unique = case.unique_kv_bytes() if config == "shared_prefix" else kv_bytes
     # fp16 (or fp32) rows in, stored rows out
     write_bytes = 2 * case.num_seqs * case.num_kv_heads * case.head_dim * (case.elt_bytes + elt)
+    dec_ms, wr_ms = primary_ms("decode"), primary_ms("write")
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9  # noqa: E731
 
     result = {
         "metric": "paged decode KV GB/s and % of MI355X HBM peak; sequences/s per layer",
@@ -440,19 +469,23 @@ def run_one(args, config):
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
-        "pa_decode": {
+        "pa_decode": {  # the whole call (both launches); figures from the cold median
             "call": ("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else "pa_decode",
-            "us": round(per_call_ms["decode"] * 1e3, 2),
-            "kv_gbs": round(kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
-            "pct_hbm_peak": round(100.0 * kv_bytes / (per_call_ms["decode"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+            "us": round(dec_ms * 1e3, 2),
+            **summary("decode"),
+            "kv_gbs": round(gbs(kv_bytes, dec_ms), 1),
+            "pct_hbm_peak": round(100.0 * gbs(kv_bytes, dec_ms) / HBM_PEAK_GBS, 2),
+            "warm_pct_hbm_peak": round(100.0 * gbs(kv_bytes, timing["decode"]["warm"]) / HBM_PEAK_GBS, 2),
             "unique_kv_bytes": unique,
-            "unique_kv_gbs": round(unique / (per_call_ms["decode"] * 1e-3) / 1e9, 1),
-            "seqs_per_s_per_layer": round(case.num_seqs / (per_call_ms["decode"] * 1e-3), 1),
+            "unique_kv_gbs": round(gbs(unique, dec_ms), 1),
+            "unique_pct_hbm_peak": round(100.0 * gbs(unique, dec_ms) / HBM_PEAK_GBS, 2),
+            "seqs_per_s_per_layer": round(case.num_seqs / (dec_ms * 1e-3), 1),
         },
         "pa_cache_write": {  # with pa_decode_append the step does not call it: timed alone
             "in_step": not fused,
-            "us": round(per_call_ms["write"] * 1e3, 2),
-            "gbs": round(write_bytes / (per_call_ms["write"] * 1e-3) / 1e9, 2),
+            "us": round(wr_ms * 1e3, 2),
+            **summary("write"),
+            "gbs": round(gbs(write_bytes, wr_ms), 2),
             "bytes": write_bytes,
         },
         "roofline": {
@@ -464,12 +497,18 @@ def run_one(args, config):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "alg_bytes_per_launch": alg_bytes,
-            "avg_launch_us": round(kern_ms_avg * 1e3, 2),
-            "cold_avg_launch_us": round(float(np.mean(cold_ms)) * 1e3, 2) if cold_ms else None,
-            "cold_achieved": round(alg_bytes / (float(np.mean(cold_ms)) * 1e-3) / 1e9, 1)
-            if cold_ms else None,
+            "timing": "cold median" if timing["kernel"]["cold"] else "warm average",
+            "launch_us": round(kern_ms * 1e3, 2),
+            **summary("kernel"),
+            "warm_achieved": round(warm_achieved, 1),
+            "warm_frac": round(warm_achieved / HBM_PEAK_GBS, 4),
         },
     }
+    if unique != kv_bytes:  # shared blocks: the bytes HBM must deliver are the unique ones
+        alg_unique = alg_bytes - kv_bytes + unique
+        result["roofline"]["unique_alg_bytes_per_launch"] = alg_unique
+        result["roofline"]["unique_achieved"] = round(gbs(alg_unique, kern_ms), 1)
+        result["roofline"]["unique_frac"] = round(gbs(alg_unique, kern_ms) / HBM_PEAK_GBS, 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(case, fp8)
     del k_cache, v_cache, ws
@@ -488,7 +527,8 @@ def prefill_cpu_baseline(case):
     n_all = int(case.query_start[1])
     ctx = int(case.context_lens[0])
     n = n_all
-    with threadpool_limits(limits=1):
+    cores = host_cores()
+    with threadpool_limits(limits=cores):
         while True:  # a prefix of sequence 0's chunk: rows 0 .. n-1 (the context cut after them)
             t0 = time.perf_counter()
             O.prefill(case.q[:n], kc, vc, case.block_tables[:1],
@@ -500,9 +540,9 @@ def prefill_cpu_baseline(case):
             n = max(8, int(n * 20.0 / dt))
     c0 = ctx - n_all  # cached tokens before the chunk
     flops = 4 * case.head_dim * case.num_q_heads * (n * c0 + n * (n + 1) // 2)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "seconds": dt, "sample": f"the first {n} of sequence 0's {n_all} chunk tokens "
-                                     "(one call), numpy float64, BLAS limited to 1 thread"}
+                                     f"(one call), numpy float64, BLAS on {cores} threads"}
 
 
 def run_prefill(args, config):
@@ -665,7 +705,8 @@ def run_block_copies(args, config):
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": round(2 * len(sub) * block_bytes / dt / 1e9, 3), "unit": "GB/s",
                                   "cores": 1, "kind": "oracle",
-                                  "sample": f"{len(sub)} block pairs within a {n_pool // 4}-block host pool"}
+                                  "sample": f"{len(sub)} block pairs within a {n_pool // 4}-block host pool "
+                                            "(numpy array copies: one thread)"}
     return result
 
 
