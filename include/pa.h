@@ -168,6 +168,58 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
                       int32_t partition_size, int32_t dtype, void* stream);
 
 /*
+ * pa_decode_shared -- pa_decode for a batch in which groups of sequences share the physical
+ * blocks of a prefix: the samples of one prompt in parallel sampling, or requests over a
+ * common cached prefix, whose tables name the same blocks by reference count ([SOSP]
+ * section 2.4; [CON] section 4.3).  The result is attention over each sequence's whole
+ * context, as pa_decode gives it, but each group's prefix is read from HBM once for all its
+ * members: the members' query heads of one kv head (up to 32 rows) are the columns of one
+ * pass over the prefix, and each member's own positions L .. ctx - 1 are a pass of its own;
+ * the second launch merges the two by log-sum-exp, in token order.  The split of the batch
+ * differs from pa_decode's, so the two agree within rounding, not bit for bit.
+ *
+ * seq_group          device, [num_seqs] int32: the group whose prefix sequence s shares, or -1
+ * group_first        device, [num_groups] int32: the group's first member; its members are the
+ *                    consecutive sequences group_first .. group_first + group_size - 1
+ * group_size         device, [num_groups] int32: members, 1 .. 32 / (num_q_heads / num_kv_heads)
+ * group_prefix       device, [num_groups] int32: shared tokens L, a positive multiple of 16 and
+ *                    of block_size, at most max_context_len and at most every member's
+ *                    context.  Positions 0 .. L - 1 of every member's table must name the
+ *                    same physical blocks: the prefix is read through the first member's
+ *                    table, the others' entries there are not read.
+ * num_groups         0 .. 65535 (0: no sharing; every sequence's seq_group must then be -1)
+ * other arguments    as pa_decode, dtype PA_F16 (q, out, pools); at most 16 query heads per kv
+ *                    head; no partition size (the default split)
+ * workspace          device, >= pa_decode_shared_workspace_bytes(...) bytes, 256-byte aligned;
+ *                    contents need no initialisation
+ *
+ * Device-side checks: as pa_decode; besides, a sequence whose group is invalid (an L not a
+ * multiple of 16 and block_size, a size out of range, members outside the batch), that is
+ * not one of its group's members, or whose context is shorter than L gets NaN rows.
+ * pa_decode_shared_partitions makes the first launch alone (the stream over the virtual
+ * sequences) and leaves the pieces in the workspace; it lets a caller time that kernel.
+ * returns PA_OK, or a negative code with nothing launched.
+ */
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim);
+int pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens,
+                     const int32_t* seq_group, const int32_t* group_first, const int32_t* group_size,
+                     const int32_t* group_prefix, int32_t num_groups, float scale, int32_t block_size,
+                     int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                     int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                     void* workspace, size_t workspace_bytes, void* stream);
+int pa_decode_shared_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const int32_t* seq_group, const int32_t* group_first,
+                                const int32_t* group_size, const int32_t* group_prefix,
+                                int32_t num_groups, float scale, int32_t block_size,
+                                int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                int64_t num_blocks, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * pa_decode_partitions / pa_decode_reduce -- the two launches pa_decode makes,
  * callable on their own (to time each kernel, or to merge pieces computed
  * elsewhere).  pa_decode_partitions takes pa_decode's arguments; it writes the rows
@@ -455,7 +507,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 7)
+#define PA_ABI_VERSION ((2 << 16) | 8)
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,9 @@ from ._lib import (  # noqa: F401
     pa_decode_noalloc,
     pa_decode_partitions,
     pa_decode_reduce,
+    pa_decode_shared,
+    pa_decode_shared_partitions,
+    pa_decode_shared_workspace_bytes,
     pa_decode_workspace_bytes,
     pa_prefill,
 )

@@ -42,6 +42,14 @@ SIGNATURES = {
     "pa_decode_noalloc": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32, _c_int32,
                                      _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int64,
                                      _c_int32, _c_int32, _vp]),
+    "pa_decode_shared_workspace_bytes": (ctypes.c_size_t, [_c_int32, _c_int32, _c_int32, _c_int32, _c_int32]),
+    "pa_decode_shared": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int32, ctypes.c_float,
+                                    _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
+                                    _c_int64, _vp, ctypes.c_size_t, _vp]),
+    "pa_decode_shared_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_int32,
+                                               ctypes.c_float, _c_int32, _c_int32, _c_int32, _c_int32,
+                                               _c_int32, _c_int32, _c_int32, _c_int64, _vp, ctypes.c_size_t,
+                                               _vp]),
     "pa_decode_partitions": (_c_int32, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _c_int32,
                                         _c_int32, _c_int32, _c_int32, _c_int32, _c_int32, _c_int32,
                                         _c_int64, _c_int32, _c_int32, _vp, ctypes.c_size_t, _vp]),
@@ -225,6 +233,57 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
         float(scale), int(block_size), int(num_kv_heads), num_seqs, num_q_heads, head_dim, max_blocks,
         int(max_context_len), k_cache.shape[0], int(partition_size), _dtype_code(q), _stream(q, stream))
     _check("pa_decode_noalloc", code)
+
+
+def pa_decode_shared_workspace_bytes(num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim) -> int:
+    return int(lib().pa_decode_shared_workspace_bytes(num_seqs, num_groups, num_q_heads, num_kv_heads,
+                                                      head_dim))
+
+
+def _shared_args(out, q, k_cache, v_cache, block_tables, context_lens, seq_group, group_first,
+                 group_size, group_prefix, scale, block_size, num_kv_heads, max_context_len, workspace,
+                 stream):
+    import torch
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_groups = group_first.shape[0]
+    max_blocks = block_tables.shape[1]
+    if max_context_len is None:
+        max_context_len = max_blocks * block_size
+    need = pa_decode_shared_workspace_bytes(num_seqs, num_groups, num_q_heads, num_kv_heads, head_dim)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(context_lens),
+            _ptr(seq_group), _ptr(group_first), _ptr(group_size), _ptr(group_prefix), int(num_groups),
+            float(scale), int(block_size), int(num_kv_heads), num_seqs, num_q_heads, head_dim, max_blocks,
+            int(max_context_len), k_cache.shape[0], ws_ptr, ws_bytes, _stream(q, stream)), workspace
+
+
+def pa_decode_shared(out, q, k_cache, v_cache, block_tables, context_lens, seq_group, group_first,
+                     group_size, group_prefix, scale, block_size, num_kv_heads, max_context_len=None,
+                     workspace=None, stream=None):
+    """pa_decode (fp16) with each group's shared prefix read once for all its members.
+
+    seq_group [S] int32 (-1: none); group_first, group_size, group_prefix [NG] int32 on the
+    device.  Returns the workspace tensor used (allocated here if none was given).
+    """
+    args, workspace = _shared_args(out, q, k_cache, v_cache, block_tables, context_lens, seq_group,
+                                   group_first, group_size, group_prefix, scale, block_size, num_kv_heads,
+                                   max_context_len, workspace, stream)
+    _check("pa_decode_shared", lib().pa_decode_shared(*args))
+    return workspace
+
+
+def pa_decode_shared_partitions(out, q, k_cache, v_cache, block_tables, context_lens, seq_group,
+                                group_first, group_size, group_prefix, scale, block_size, num_kv_heads,
+                                max_context_len=None, workspace=None, stream=None):
+    """First launch of pa_decode_shared alone (the stream over the virtual sequences)."""
+    args, workspace = _shared_args(out, q, k_cache, v_cache, block_tables, context_lens, seq_group,
+                                   group_first, group_size, group_prefix, scale, block_size, num_kv_heads,
+                                   max_context_len, workspace, stream)
+    _check("pa_decode_shared_partitions", lib().pa_decode_shared_partitions(*args))
+    return workspace
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,

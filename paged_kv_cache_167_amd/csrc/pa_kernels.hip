@@ -607,6 +607,58 @@ __device__ __forceinline__ void merge_row(T* dst, const float* rec_m, const floa
   for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(num[k] / den);
 }
 
+// The merge of merge_row over any list of pieces: piece p's running max, exp-sum and
+// normalised output are record row idx(p) (record * rows per record + row), pieces in token
+// order; the same arithmetic, in the same order.
+template <typename T, int D, typename Idx>
+__device__ __forceinline__ void merge_indexed(T* dst, const float* rec_m, const float* rec_l, const float* rec_o,
+                                              int npieces, Idx idx, int lane) {
+  constexpr int kDPL = D / kWave;
+  constexpr int kU = 4;
+  auto out_of = [&](int p) { return rec_o + static_cast<int64_t>(idx(p)) * D; };
+  float big_m = -INFINITY, den = 0.0f;
+  float num[kDPL];
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) num[k] = 0.0f;
+  for (int p0 = 0; p0 < npieces; p0 += kWave) {
+    const int p = p0 + lane;
+    const int cnt = min(kWave, npieces - p0);
+    const int r = p < npieces ? idx(p) : 0;
+    const float mp = p < npieces ? rec_m[r] : -INFINITY;
+    const float lp = p < npieces ? rec_l[r] : 0.0f;
+    float ov[kU][kDPL];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int k = 0; k < kDPL; ++k) ov[u][k] = u < cnt ? out_of(p0 + u)[k * kWave + lane] : 0.0f;
+    const float m_new = fmaxf(big_m, wave_max(mp));
+    const float c_old = rescale(big_m, m_new);
+    const float wp = p < npieces ? lp * __builtin_amdgcn_exp2f(mp - m_new) : 0.0f;
+    den = den * c_old + wave_sum(wp);
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) num[k] *= c_old;
+    for (int i = 0; i < cnt; i += kU) {
+      if (i > 0) {
+#pragma unroll
+        for (int u = 0; u < kU; ++u)
+#pragma unroll
+          for (int k = 0; k < kDPL; ++k) ov[u][k] = i + u < cnt ? out_of(p0 + i + u)[k * kWave + lane] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (i + u < cnt) {
+          const float wgt = as_f(__builtin_amdgcn_readlane(as_u(wp), i + u));
+#pragma unroll
+          for (int k = 0; k < kDPL; ++k) num[k] = fmaf(wgt, ov[u][k], num[k]);
+        }
+      }
+    }
+    big_m = m_new;
+  }
+#pragma unroll
+  for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(num[k] / den);
+}
+
 template <typename T, int D, int GT>
 __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   using K = Cfg<T, D, GT>;
@@ -1812,6 +1864,542 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
 }
 
 // ---------------------------------------------------------------------------
+// decode with shared prefixes (pa_decode_shared): groups of sequences whose tables hold the
+// same physical blocks for their first L tokens (parallel samples of one prompt, requests
+// that share a cached prefix; [SOSP] section 2.4 and [CON] section 4.3 share such blocks by
+// reference counts).  The batch becomes a list of virtual sequences: first each group's
+// prefix, whose query rows are the query heads of all its members (at most kShRows per kv
+// head), then each sequence's own part, positions L .. ctx - 1.  A prefix is streamed once
+// for all its members; every piece goes to a record, and the reduce merges, per query row,
+// the pieces of its group's prefix and then those of its own part, in token order.
+// ---------------------------------------------------------------------------
+
+struct SharedArgs {
+  const int32_t* seq_group;     // [S] the group whose prefix sequence s shares, -1: none
+  const int32_t* group_first;   // [NG] first member (the members are consecutive sequences)
+  const int32_t* group_size;    // [NG] members
+  const int32_t* group_prefix;  // [NG] shared tokens L
+  int num_groups;
+};
+
+constexpr int kShRows = 32;         // query rows of a prefix per kv head: two 16-row blocks
+constexpr int kShWavesPerCU = 3;    // its 16 KB stages (q area doubled) fit three rings per CU
+
+// Whether group gi describes a prefix the kernels can stream: L whole tiles and whole blocks,
+// at most max_ctx, 1 .. kShRows / group members that are sequences of the batch.
+__device__ __forceinline__ bool shared_group_ok(int L, int n, int f, int S, int group, int bsz, int max_ctx) {
+  return L > 0 && L <= max_ctx && L % 16 == 0 && L % bsz == 0 && n >= 1 && n * group <= kShRows && f >= 0 &&
+         f <= S - n;
+}
+
+// Position of a wave in the list of virtual sequences (all wave-uniform).
+struct VCursor {
+  int v;       // virtual sequence: group v's prefix (v < NG), else sequence v - NG's own part
+  int unit;    // kv head
+  int t, nt;   // tile within the segment, tiles in it
+  int ctx;     // tokens of the virtual sequence
+  int gstart;  // global index of the segment's first tile
+  int trow;    // block-table row it reads
+  int pos0;    // position of its first token in that row
+  int s0;      // sequence of its first query row
+  int rows;    // query rows per kv head (members x group, or group)
+};
+
+template <int TK>
+struct VWork {
+  const int32_t* ctxs;
+  SharedArgs sh;
+  int S, NG, V, max_ctx, n_units, G, bsz;
+  int Q, R, A, n_my;
+
+  __device__ static int tiles(int c) { return c > 0 ? (c + TK - 1) / TK : 0; }
+
+  // Virtual sequence v: its tokens, table row, first position, first query sequence and
+  // query rows per kv head.  LOAD reads one 32-bit element (vector loads for the
+  // lane-parallel scans, scalar loads for the cursor).  Tokens are 0 (nothing streamed)
+  // for an invalid group, a prefix of no valid group, or an own part that is invalid; the
+  // reduce gives the affected rows NaN.
+  template <typename Load>
+  __device__ void geom(int v, Load load, int& ctxv, int& trow, int& pos0, int& s0, int& rows) const {
+    if (v < NG) {
+      const int L = load(sh.group_prefix + v), n = load(sh.group_size + v), f = load(sh.group_first + v);
+      const bool ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx);
+      ctxv = ok ? L : 0;
+      trow = ok ? f : 0;
+      pos0 = 0;
+      s0 = trow;
+      rows = ok ? n * G : G;
+    } else {
+      const int s = v - NG;
+      const int c = load(ctxs + s);
+      const int gi = load(sh.seq_group + s);
+      int L = 0;
+      bool ok = c > 0 && c <= max_ctx;
+      if (gi >= 0) {
+        ok = ok && gi < NG;
+        if (ok) {  // the group arrays are read only at valid indexes (they may be empty)
+          L = load(sh.group_prefix + gi);
+          const int n = load(sh.group_size + gi), f = load(sh.group_first + gi);
+          ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx) && s >= f && s < f + n && L <= c;
+        }
+      }
+      ctxv = ok ? c - L : 0;
+      trow = s;
+      pos0 = ok ? L : 0;
+      s0 = s;
+      rows = G;
+    }
+  }
+
+  __device__ void init(const StreamArgs& a, const SharedArgs& shv, int w, int lane, int bs) {
+    ctxs = a.context_lens;
+    sh = shv;
+    S = a.num_seqs;
+    NG = sh.num_groups;
+    V = NG + S;
+    max_ctx = a.max_context_len;
+    n_units = a.num_kv_heads;
+    G = a.group;
+    bsz = bs;
+    const auto vload = [](const int32_t* p) { return *p; };
+    int part = 0;
+    for (int b = 0; b < V; b += kWave) {
+      if (b + lane < V) {
+        int cv, tr, p0, s0, rw;
+        geom(b + lane, vload, cv, tr, p0, s0, rw);
+        part += tiles(cv);
+      }
+    }
+    const int total = wave_sum_int(part) * n_units;
+    Q = total / a.num_waves;
+    R = total - Q * a.num_waves;
+    A = w * Q + min(w, R);
+    n_my = Q + (w < R ? 1 : 0);
+  }
+
+  __device__ int wave_of(int x) const {
+    const int cut = R * (Q + 1);
+    return (x < cut || Q == 0) ? x / (Q + 1) : R + (x - cut) / Q;
+  }
+
+  __device__ void set(VCursor& c, int v) const {
+    c.v = v;
+    geom(v, [](const int32_t* p) { return scalar_load(p); }, c.ctx, c.trow, c.pos0, c.s0, c.rows);
+    c.nt = tiles(c.ctx);
+  }
+
+  // cursor at global tile x (below the total)
+  __device__ VCursor locate(int x, int lane) const {
+    const auto vload = [](const int32_t* p) { return *p; };
+    int v0 = 0, base = 0;
+    for (int b = 0; b < V; b += kWave) {
+      int cv = 0, tr, p0, s0, rw;
+      if (b + lane < V) geom(b + lane, vload, cv, tr, p0, s0, rw);
+      const int ts = tiles(cv) * n_units;
+      const int incl = wave_incl_scan_int(ts, lane);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > x);
+      if (hit != 0) {
+        const int l = __builtin_ctzll(hit);
+        v0 = b + l;
+        base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
+        break;
+      }
+      base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    }
+    VCursor c;
+    set(c, v0);
+    c.unit = (x - base) / c.nt;
+    c.t = (x - base) - c.unit * c.nt;
+    c.gstart = base + c.unit * c.nt;
+    return c;
+  }
+
+  __device__ void advance(VCursor& c) const {
+    if (++c.t < c.nt) return;
+    c.gstart += c.nt;
+    c.t = 0;
+    if (++c.unit < n_units) return;
+    c.unit = 0;
+    do {
+      if (c.v + 1 >= V) {
+        c.v = V;
+        c.nt = 0;
+        c.ctx = 0;
+        break;
+      }
+      set(c, c.v + 1);
+    } while (c.nt == 0);
+  }
+};
+
+// The shared-prefix stream kernel: the fp16 MFMA stream kernel (3-stage ring, persistent
+// waves, equal shares of the tile list) over the virtual sequences, with up to two 16-row
+// blocks of query rows per unit (NRB) and every piece written to a record.
+template <int D>
+__global__ __launch_bounds__(kWave) void pa_shared_mfma_kernel(const StreamArgs a, const SharedArgs sh) {
+  using K = MCfg<D, false>;
+  constexpr int NST = kMfStages;
+  constexpr int TK = K::kTK, KB = K::kKB, NB = K::kNB, NC = K::kNC, ROW = K::kRow;
+  constexpr int ROWQ = K::kRowQ, NCQ = K::kNCQ;
+  constexpr int LOADS = K::kLoads, HALF = K::kHalf;
+  constexpr int NRB = kShRows / kMfRows;        // row blocks per unit
+  constexpr int STAGE = 2 * HALF + kShRows * ROWQ;
+  constexpr int QOFF = 2 * HALF;
+  constexpr int QROWS = 1024 / ROWQ;
+  constexpr int VM = (NST - 1) * 2 * LOADS;
+  static_assert(VM <= 63, "vmcnt range");
+  static_assert(NST * STAGE <= 65536, "stage offsets are 16-bit immediates");
+  __shared__ __align__(1024) char s_ring[NST * STAGE];
+
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int g = lane % 16;
+  const int jq = lane / 16;
+  const int bsz = a.block_size;
+
+  VWork<TK> wk;
+  wk.init(a, sh, w, lane, bsz);
+  const int n_my = wk.n_my;
+  if (n_my == 0) return;
+  const int A = wk.A, A_end = A + n_my;
+  VCursor cc = wk.locate(A, lane);
+
+  const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
+  uint32_t ka[KB], va[NB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int c = jq * KB + kb;
+    ka[kb] = ring + static_cast<uint32_t>(g * ROW + ((c ^ swz16<D>(g)) * 16));
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = 4 * jq + (g >> 2), q = g & 3;
+    const int c = 2 * nb + (q >> 1);
+    va[nb] = ring + static_cast<uint32_t>(HALF + r * ROW + ((c ^ swz16<D>(r)) * 16) + (q & 1) * 8);
+  }
+  const uint32_t qa = ring + static_cast<uint32_t>(g * ROWQ + jq * KB * 16);  // block rb: + 16 rb ROWQ
+  uint32_t lo[LOADS];
+  bool hi8[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int pos = i * 64 + lane;
+    const int r = pos / NC, p = pos % NC;
+    const int rr = bsz >= TK ? r : (r & (bsz - 1));
+    lo[i] = static_cast<uint32_t>(rr * ROW + ((p ^ swz16<D>(r)) * 16));
+    hi8[i] = r >= 8;
+  }
+
+  const char* kcache = static_cast<const char*>(a.k_cache);
+  const char* vcache = static_cast<const char*>(a.v_cache);
+  const char* qbytes = static_cast<const char*>(a.q);
+  const uint64_t head_bytes = static_cast<uint64_t>(bsz) * ROW;
+  const uint64_t block_bytes = head_bytes * static_cast<uint64_t>(a.num_kv_heads);
+  const int G = a.group;
+
+  // table entries of tile f: its first row slot's and, for block size 8, the second half's
+  auto entry_ptrs = [&](const VCursor& f, bool real, const int32_t*& e0, const int32_t*& e1)
+      __attribute__((always_inline)) {
+    if (!real) {
+      e0 = e1 = uniform_ptr(a.block_tables);
+      return;
+    }
+    const int tok0 = f.t * TK;
+    const int32_t* p = a.block_tables + static_cast<int64_t>(f.trow) * a.max_blocks_per_seq +
+                       ((f.pos0 + tok0) >> a.log2_block);
+    e0 = uniform_ptr(p);
+    e1 = (bsz < TK && tok0 + bsz < f.ctx) ? uniform_ptr(p + 1) : e0;
+  };
+
+  auto fetch = [&](const VCursor& f, bool real, bool qload, int st, int p0, int p1)
+      __attribute__((always_inline)) -> bool {
+    bool bad = false;
+    const int kvh = real ? f.unit : 0;
+    const int tok0 = f.t * TK;
+    if (real) {
+      if (p0 < 0 || p0 >= a.num_blocks) {
+        bad = true;
+        p0 = 0;
+      }
+      if (bsz < TK && tok0 + bsz < f.ctx) {
+        if (p1 < 0 || p1 >= a.num_blocks) {
+          bad = true;
+          p1 = 0;
+        }
+      } else {
+        p1 = 0;
+      }
+    } else {
+      p0 = 0;
+      p1 = 0;
+    }
+    char* stage = s_ring + st * STAGE;
+    if (qload) {  // rows r < f.rows: member r / G's query head kvh G + r % G
+#pragma unroll
+      for (int i = 0; i < kShRows / QROWS; ++i) {
+        if (i * QROWS < f.rows) {
+          const int r = min(i * QROWS + lane / NCQ, f.rows - 1);
+          const int64_t qrow = static_cast<int64_t>(f.s0 + r / G) * a.num_q_heads + kvh * G + r % G;
+          __builtin_amdgcn_global_load_lds(qbytes + qrow * ROWQ + (lane % NCQ) * 16, stage + QOFF + i * 1024, 16, 0,
+                                           0);
+        }
+      }
+    }
+    const uint64_t head = static_cast<uint64_t>(kvh) * head_bytes;
+    const uint64_t b0 = static_cast<uint64_t>(static_cast<uint32_t>(p0)) * block_bytes + head +
+                        static_cast<uint64_t>((f.pos0 + tok0) & (bsz - 1)) * ROW * (real ? 1 : 0);
+    const uint64_t b1 = static_cast<uint64_t>(static_cast<uint32_t>(p1)) * block_bytes + head;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const bool second = bsz < TK && (K::kRowsPerLoad > 8 ? hi8[i] : i * K::kRowsPerLoad >= 8);
+      const uint64_t off = (second ? b1 : b0) + lo[i];
+      __builtin_amdgcn_global_load_lds(kcache + off, stage + i * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vcache + off, stage + HALF + i * 1024, 16, 0, 0);
+    }
+    return bad;
+  };
+
+  f16x8 qop[NRB][KB];
+  f32x4 o[NRB][NB];
+  float m[NRB], l[NRB];
+  int rows = 0;
+  bool piece_bad = false;
+
+  auto piece_start = [&](auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    rows = cc.rows;
+    unroll<NRB>([&](auto rbc) __attribute__((always_inline)) {
+      constexpr int rb = decltype(rbc)::value;
+      if (rb == 0 || rows > 16) {
+        read_q_mf<KB, st * STAGE + QOFF + rb * 16 * ROWQ>(qa, qop[rb]);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qop[rb][kb] = 16 * rb + g < rows ? qop[rb][kb] : f16x8{};
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qop[rb][kb] = f16x8{};
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[rb][nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      m[rb] = -INFINITY;
+      l[rb] = 0.0f;
+    });
+    piece_bad = false;
+    if (cc.t == 0 && lane == 0)
+      a.seg_desc[cc.v * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+  };
+
+  auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
+    constexpr float kRebase = 8.0f;
+    const bool full = cn >= TK;
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ok[i] = full || (4 * jq + i < cn);
+    if (!full) {  // V rows past the context (poison or block 0) must not reach O
+      const uint32_t mlo = (ok[0] ? 0x0000FFFFu : 0u) | (ok[1] ? 0xFFFF0000u : 0u);
+      const uint32_t mhi = (ok[2] ? 0x0000FFFFu : 0u) | (ok[3] ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        uint64_t x = __builtin_bit_cast(uint64_t, vop[nb]);
+        x &= (static_cast<uint64_t>(mhi) << 32) | mlo;
+        vop[nb] = __builtin_bit_cast(f16x4, x);
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (rb > 0 && rows <= 16) break;  // wave-uniform: one row block
+      f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        if (kb & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[rb][kb], sb, 0, 0, 0);
+        else sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[rb][kb], sa, 0, 0, 0);
+      }
+      const f32x4 sc = sa + sb;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt = fmaxf(mt, ok[i] ? sc[i] : -INFINITY);
+      {
+        const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(mt), as_u(mt), false, false);
+        mt = fmaxf(as_f(x32[0]), as_f(x32[1]));
+        const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(mt), as_u(mt), false, false);
+        mt = fmaxf(as_f(x16[0]), as_f(x16[1]));
+      }
+      mt *= a.scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m[rb] + kRebase) != 0) {
+        const float m_new = fmaxf(m[rb], mt);
+        const float corr = rescale(m[rb], m_new);
+        l[rb] *= corr;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[rb][nb] *= corr;
+        m[rb] = m_new;
+      }
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = ok[i] ? __builtin_amdgcn_exp2f(fmaf(sc[i], a.scale_log2, -m[rb])) : 0.0f;
+        l[rb] += p[i];
+      }
+      const f16x4 pb = {static_cast<f16>(p[0]), static_cast<f16>(p[1]), static_cast<f16>(p[2]),
+                        static_cast<f16>(p[3])};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        o[rb][nb] = __builtin_amdgcn_mfma_f32_16x16x16f16(vop[nb], pb, o[rb][nb], 0, 0, 0);
+    }
+  };
+
+  // every piece ends in a record (rows 16 rb + g < rows of each row block): a segment held
+  // whole by this wave in the record of its own after the waves' (a share may hold several),
+  // a split one in this wave's head or tail record
+  auto piece_end = [&]() __attribute__((always_inline)) {
+    const bool head = cc.gstart < A;
+    const bool whole = !head && cc.gstart + cc.nt <= A_end;
+    const int rec = whole ? 2 * a.num_waves + cc.v * a.n_units + cc.unit : w * 2 + (head ? 0 : 1);
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (rb > 0 && rows <= 16) break;
+      float lt = l[rb];
+      {
+        const auto x32 = __builtin_amdgcn_permlane32_swap(as_u(lt), as_u(lt), false, false);
+        lt = as_f(x32[0]) + as_f(x32[1]);
+        const auto x16 = __builtin_amdgcn_permlane16_swap(as_u(lt), as_u(lt), false, false);
+        lt = as_f(x16[0]) + as_f(x16[1]);
+      }
+      const int row = 16 * rb + g;
+      if (row < rows) {
+        const float inv = piece_bad ? qnan : 1.0f / lt;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int col = 16 * nb + 4 * jq;
+          const f32x4 y = o[rb][nb] * inv;
+          *reinterpret_cast<f32x4*>(a.rec_o + (static_cast<int64_t>(rec) * a.rec_rows + row) * D + col) = y;
+        }
+        if (jq == 0) {
+          a.rec_m[rec * a.rec_rows + row] = piece_bad ? qnan : m[rb];
+          a.rec_l[rec * a.rec_rows + row] = piece_bad ? qnan : lt;
+        }
+      }
+    }
+  };
+
+  f16x8 kop[KB];
+  f16x4 vop[NB];
+  bool fbad[NST];
+  auto process = [&](int i, auto stc) __attribute__((always_inline)) {
+    constexpr int st = decltype(stc)::value;
+    if (i == 0 || cc.t == 0) piece_start(stc);
+    piece_bad |= fbad[st];
+    consume(min(TK, cc.ctx - cc.t * TK), kop, vop);
+    if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
+    wk.advance(cc);
+  };
+
+  VCursor cf = cc;
+  const int32_t *e0, *e1;
+  int32_t pe0 = 0, pe1 = 0;
+  {
+    VCursor c1 = cf;
+    wk.advance(c1);
+    VCursor c2 = c1;
+    wk.advance(c2);
+    const int32_t *a0, *a1, *b0, *b1;
+    entry_ptrs(cf, true, a0, a1);
+    entry_ptrs(c1, 1 < n_my, b0, b1);
+    entry_ptrs(c2, 2 < n_my, e0, e1);
+    int32_t p[6];
+    load_entries6(uniform_ptr(a0), uniform_ptr(a1), uniform_ptr(b0), uniform_ptr(b1), uniform_ptr(e0),
+                  uniform_ptr(e1), p);
+    fbad[0] = fetch(cf, true, true, 0, p[0], p[1]);
+    fbad[1] = fetch(c1, 1 < n_my, 1 < n_my && c1.t == 0, 1, p[2], p[3]);
+    cf = c2;
+    pe0 = p[4];
+    pe1 = p[5];
+  }
+  static_assert(NST == 3, "the prologue fills two stages");
+  for (int i0 = 0; i0 < n_my; i0 += NST) {
+    unroll<NST>([&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int nxt = (st + NST - 1) % NST;
+      const int i = i0 + st;
+      const bool real = i + NST - 1 < n_my;
+      fbad[nxt] = fetch(cf, real, real && cf.t == 0, nxt, pe0, pe1);
+      wk.advance(cf);
+      entry_ptrs(cf, i + NST < n_my, e0, e1);
+      read_stage_mf<D, VM, st * STAGE>(ka, va, kop, vop, e0, e1, pe0, pe1);
+      if (i < n_my) process(i, stc);
+    });
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load still writes LDS at exit
+}
+
+// The reduce of pa_decode_shared: one wave per (sequence, query head).  Row (s, h) merges,
+// in token order, the pieces of its group's prefix segment (row (s - first) G + h % G of
+// those records) and the pieces of its own part (row h % G); zero for an empty context, NaN
+// for an invalid one or an invalid group.
+template <int D>
+__global__ __launch_bounds__(kWave) void pa_shared_reduce_kernel(f16* __restrict__ out, const int2* __restrict__ seg_desc,
+                                                                 const float* __restrict__ rec_m,
+                                                                 const float* __restrict__ rec_l,
+                                                                 const float* __restrict__ rec_o,
+                                                                 const int32_t* __restrict__ context_lens,
+                                                                 const SharedArgs sh, int num_seqs, int num_q_heads,
+                                                                 int group, int n_units, int max_context_len,
+                                                                 int block_size, int waves, int rec_rows) {
+  constexpr int kDPL = D / kWave;
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int lane = threadIdx.x;
+  f16* dst = out + (static_cast<int64_t>(s) * num_q_heads + h) * D;
+  const int kvh = h / group, hg = h - kvh * group;
+  const int NG = sh.num_groups;
+  const int ctx = context_lens[s];
+  const int gi = sh.seq_group[s];
+  bool ok = ctx >= 0 && ctx <= max_context_len;
+  int L = 0, f = 0;
+  if (gi >= 0) {
+    ok = ok && gi < NG;
+    if (ok) {  // the group arrays are read only at valid indexes (they may be empty)
+      L = sh.group_prefix[gi];
+      const int n = sh.group_size[gi];
+      f = sh.group_first[gi];
+      ok = shared_group_ok(L, n, f, num_seqs, group, block_size, max_context_len) && s >= f && s < f + n &&
+           L <= ctx;
+    }
+  }
+  if (!ok) {
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<f16>(__builtin_nanf(""));
+    return;
+  }
+  if (ctx == 0) {
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<f16>(0.0f);
+    return;
+  }
+  // the two lists of pieces: the prefix segment (group gi, row (s - f) G + hg) and the own
+  // segment (sequence s, row hg); a segment held whole by one wave has one piece, in the
+  // record 2 waves + its segment index
+  const int sp = gi * n_units + kvh, so = (NG + s) * n_units + kvh;
+  const int2 dp = gi >= 0 ? seg_desc[sp] : make_int2(0, -1);
+  const int2 dn = ctx > L ? seg_desc[so] : make_int2(0, -1);
+  const int np0 = dp.y - dp.x + 1, np1 = dn.y - dn.x + 1;
+  const bool desc_ok = (gi < 0 || (dp.x >= 0 && dp.x <= dp.y && dp.y < waves)) &&
+                       (ctx <= L || (dn.x >= 0 && dn.x <= dn.y && dn.y < waves));
+  if (!desc_ok) {  // not written by the stream kernel
+#pragma unroll
+    for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<f16>(__builtin_nanf(""));
+    return;
+  }
+  const int rp = (s - f) * group + hg;
+  auto idx = [&](int p) {  // flat record row of piece p, in token order
+    const bool pre = p < np0;
+    const int q = pre ? p : p - np0;
+    const int2 d = pre ? dp : dn;
+    const int rec = d.x == d.y ? 2 * waves + (pre ? sp : so) : (q == 0 ? d.x * 2 + 1 : (d.x + q) * 2);
+    return rec * rec_rows + (pre ? rp : hg);
+  };
+  merge_indexed<f16, D>(dst, rec_m, rec_l, rec_o, np0 + np1, idx, lane);
+}
+
+// ---------------------------------------------------------------------------
 // Several query tokens per sequence: causal attention of a prompt chunk over the paged
 // cache.  Sequence s has n = query_start[s+1] - query_start[s] query tokens, the last n
 // positions of its context; query i (position ctx - n + i) sees positions 0 .. ctx - n + i.
@@ -2862,6 +3450,89 @@ DecodeCall make_call(void* out, const void* q, const void* k_cache, const void* 
   return c;
 }
 
+// ---- pa_decode_shared: geometry, checks, launches
+
+// Workspace of pa_decode_shared: a descriptor per (virtual sequence, kv head), and records
+// of kShRows rows: two per wave (of at most kMaxWaves) for split segments, one per segment
+// for segments held whole by one wave.
+Geom shared_geometry(int64_t num_seqs, int64_t num_groups, int num_kv_heads, int head_dim) {
+  Geom g;
+  g.gt = kMfRows;
+  g.n_gtiles = 1;
+  g.n_units = num_kv_heads;
+  g.rec_rows = kShRows;
+  g.w_cap = kMaxWaves;
+  const int64_t segs = (num_groups + num_seqs) * num_kv_heads;
+  const int64_t recs = 2 * static_cast<int64_t>(g.w_cap) + segs;
+  g.desc_bytes = align256(static_cast<size_t>(segs) * 2 * sizeof(int));
+  g.rec_ml_bytes = align256(static_cast<size_t>(recs) * g.rec_rows * sizeof(float));
+  g.rec_o_bytes = align256(static_cast<size_t>(recs) * g.rec_rows * head_dim * sizeof(float));
+  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
+  return g;
+}
+
+// launches: bit 0 the stream kernel, bit 1 the reduce
+template <int D>
+int launch_shared(const DecodeCall& c, const Geom& g, const SharedArgs& sh, int launches) {
+  const Residency r = residency(reinterpret_cast<const void*>(pa_shared_mfma_kernel<D>));
+  if (r.waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_shared_mfma_kernel failed");
+  int64_t waves = static_cast<int64_t>(r.cus) * kShWavesPerCU;
+  if (waves > r.waves) waves = r.waves;
+  if (waves > g.w_cap) waves = g.w_cap;
+  StreamArgs a = stream_args(c, g);
+  a.num_waves = static_cast<int>(waves);
+  if (launches & 1) {
+    hipLaunchKernelGGL((pa_shared_mfma_kernel<D>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a, sh);
+    const int rc = check_hip("pa_shared_mfma_kernel launch");
+    if (rc != PA_OK) return rc;
+  }
+  if (launches & 2) {
+    const WsParts ws = split_workspace(c.workspace, g);
+    hipLaunchKernelGGL((pa_shared_reduce_kernel<D>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0, c.stream,
+                       static_cast<f16*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o, c.context_lens, sh,
+                       c.num_seqs, c.num_q_heads, c.num_q_heads / c.num_kv_heads, g.n_units, c.max_context_len,
+                       c.block_size, a.num_waves, g.rec_rows);
+    return check_hip("pa_shared_reduce_kernel launch");
+  }
+  return PA_OK;
+}
+
+int decode_shared(int launches, void* out, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_group,
+                  const int32_t* group_first, const int32_t* group_size, const int32_t* group_prefix,
+                  int32_t num_groups, float scale, int32_t block_size, int32_t num_kv_heads, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int64_t num_blocks, void* workspace, size_t workspace_bytes, void* stream) {
+  g_error.clear();
+  DecodeCall c = make_call(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, num_kv_heads,
+                           num_seqs, num_q_heads, head_dim, max_blocks_per_seq, max_context_len, num_blocks, 0,
+                           PA_F16, workspace, workspace_bytes, stream);
+  Geom g0;
+  int rc = check_decode(c, &g0, false);
+  if (rc != PA_OK) return rc;
+  if (num_q_heads / num_kv_heads > kMfRows)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode_shared: %d query heads per kv head, at most %d",
+                num_q_heads / num_kv_heads, kMfRows);
+  if (num_groups < 0 || num_groups > 65535)
+    return fail(PA_ERR_INVALID_ARG, "num_groups %d outside [0, 65535]", num_groups);
+  if ((static_cast<int64_t>(num_seqs) + num_groups) * num_kv_heads *
+          std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + 7) / 8) >
+      (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
+  if (num_seqs == 0) return PA_OK;
+  if (!seq_group || (num_groups > 0 && (!group_first || !group_size || !group_prefix)))
+    return fail(PA_ERR_INVALID_ARG, "a group array is NULL");
+  if (!aligned(seq_group, 4) || !aligned(group_first, 4) || !aligned(group_size, 4) || !aligned(group_prefix, 4))
+    return fail(PA_ERR_INVALID_ARG, "the group arrays must be 4-byte aligned");
+  const Geom g = shared_geometry(num_seqs, num_groups, num_kv_heads, head_dim);
+  if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);
+  if (workspace_bytes < g.ws_bytes)
+    return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, g.ws_bytes);
+  if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const SharedArgs sh{seq_group, group_first, group_size, group_prefix, num_groups};
+  return head_dim == 64 ? launch_shared<64>(c, g, sh, launches) : launch_shared<128>(c, g, sh, launches);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -3260,6 +3931,37 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   a.n_row_blocks = 0;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   return head_dim == 64 ? launch_prefill<64>(a, rows, num_seqs, st) : launch_prefill<128>(a, rows, num_seqs, st);
+}
+
+size_t pa_decode_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim) {
+  if (num_seqs <= 0 || num_groups < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return 0;
+  return shared_geometry(num_seqs, num_groups, num_kv_heads, head_dim).ws_bytes;
+}
+
+int pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     const int32_t* context_lens, const int32_t* seq_group, const int32_t* group_first,
+                     const int32_t* group_size, const int32_t* group_prefix, int32_t num_groups, float scale,
+                     int32_t block_size, int32_t num_kv_heads, int32_t num_seqs, int32_t num_q_heads,
+                     int32_t head_dim, int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_shared(3, out, q, k_cache, v_cache, block_tables, context_lens, seq_group, group_first, group_size,
+                       group_prefix, num_groups, scale, block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                       max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
+}
+
+int pa_decode_shared_partitions(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, const int32_t* context_lens, const int32_t* seq_group,
+                                const int32_t* group_first, const int32_t* group_size, const int32_t* group_prefix,
+                                int32_t num_groups, float scale, int32_t block_size, int32_t num_kv_heads,
+                                int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_blocks_per_seq,
+                                int32_t max_context_len, int64_t num_blocks, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return decode_shared(1, out, q, k_cache, v_cache, block_tables, context_lens, seq_group, group_first, group_size,
+                       group_prefix, num_groups, scale, block_size, num_kv_heads, num_seqs, num_q_heads, head_dim,
+                       max_blocks_per_seq, max_context_len, num_blocks, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

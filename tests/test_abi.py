@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 7
+    assert P.lib().pa_abi_version() == (2 << 16) | 8
 
 
 def test_workspace_size_query():

@@ -238,7 +238,7 @@ def _assemble(name, dtype, num_q_heads, num_kv_heads, head_dim, block_size, num_
     shared_of = meta.pop("_shared_of", None)
     seq_rows = []
     for s in range(num_seqs):
-        parts = [] if shared_of is None else [extra_rows[shared_of[s]]]
+        parts = [] if shared_of is None or shared_of[s] < 0 else [extra_rows[shared_of[s]]]
         parts.append(own_rows[s])
         seq_rows.append(np.concatenate(parts))
     meta["seq_rows"] = seq_rows
@@ -440,6 +440,95 @@ def shared_prefix(variant="plain", num_prompts=16, samples=8, prompt_len=2000,
             "_shared_of": [s // samples for s in range(len(ctx))]}
     return _assemble("shared_prefix", dtype, hq, hkv, d, B, num_blocks, 1.0 / np.sqrt(d), ctx,
                      tables, q, seq_tokens, alloc.refcount, meta)
+
+
+def shared_groups(layout, seed=2024, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16,
+                  dtype=np.float16, sigma=0.5, variant="plain") -> PagedDecodeCase:
+    """A batch of prefix-sharing groups and independent sequences, in the order of ``layout``.
+
+    Each item is ("g", prompt_len, tails): a group of len(tails) sequences whose tables hold
+    the same physical blocks for the prompt_len prompt tokens (a multiple of block_size),
+    each with a private tail of that many tokens plus the token it appends this step
+    (ctx = prompt_len + tail + 1); or ("s", ctx): an independent sequence.  meta holds the
+    group arrays pa_decode_shared takes: "seq_group" [S], "group_first", "group_size",
+    "group_prefix" [NG].
+    """
+    B, d = block_size, head_dim
+    group = num_q_heads // num_kv_heads
+    ctx, seq_group, groups = [], [], []
+    for item in layout:
+        if item[0] == "g":
+            _, plen, tails = item
+            assert plen % B == 0 and plen > 0
+            groups.append((len(ctx), len(tails), plen))
+            for t in tails:
+                ctx.append(plen + int(t) + 1)
+                seq_group.append(len(groups) - 1)
+        else:
+            ctx.append(int(item[1]))
+            seq_group.append(-1)
+    ctx = np.asarray(ctx, dtype=np.int64)
+    own_blocks = []
+    for s, c in enumerate(ctx):
+        gi = seq_group[s]
+        plen = groups[gi][2] if gi >= 0 else 0
+        own_blocks.append(int(-(-int(c) // B)) - plen // B)
+    needed = sum(g[2] // B for g in groups) + sum(own_blocks)
+    num_blocks = max(4, int(np.ceil(1.3 * needed)) + 2)
+    alloc = BlockAllocator(num_blocks, np.random.default_rng([seed, 7, B]))
+    width = int(max(-(-int(c) // B) for c in ctx)) + 1
+    tables = np.full((len(ctx), width), -1, dtype=np.int32)
+    q = _normal(np.random.default_rng([seed, 0]), (len(ctx), num_q_heads, d), sigma, dtype)
+    denom = float(ctx.max())
+    extra, gblocks = [], []
+    for gi, (first, size, plen) in enumerate(groups):
+        prng = np.random.default_rng([seed, 2, gi])
+        pk = _normal(prng, (plen, num_kv_heads, d), sigma, dtype)
+        pv = _normal(prng, (plen, num_kv_heads, d), sigma, dtype)
+        if variant == "poscode":
+            _poscode(pv, 0, denom, dtype)
+        pblocks = [alloc.allocate() for _ in range(plen // B)]
+        for b in pblocks:
+            for _ in range(size - 1):
+                alloc.share(b)
+        extra.append((pk, pv, _slots(np.asarray(pblocks), np.arange(plen), B)))
+        gblocks.append(pblocks)
+    needle_rng = np.random.default_rng([seed, 9])
+    seq_tokens = []
+    for s, c in enumerate(ctx):
+        c = int(c)
+        gi = seq_group[s]
+        plen = groups[gi][2] if gi >= 0 else 0
+        if gi >= 0:
+            tables[s, :plen // B] = gblocks[gi]
+        for j in range(plen // B, -(-c // B)):
+            tables[s, j] = alloc.allocate()
+        trng = np.random.default_rng([seed, 3, s])
+        n_own = c - plen
+        tk = _normal(trng, (n_own, num_kv_heads, d), sigma, dtype)
+        tv = _normal(trng, (n_own, num_kv_heads, d), sigma, dtype)
+        if variant == "needle":
+            _plant_needle(tk, q[s], int(needle_rng.integers(0, n_own)), group, dtype)
+        elif variant == "poscode":
+            _poscode(tv, plen, denom, dtype)
+        seq_tokens.append((tk, tv, _slots(tables[s], np.arange(plen, c), B)))
+    meta = {"variant": variant, "seed": seed, "sigma": sigma, "_extra_prefix": extra,
+            "_shared_of": list(seq_group),
+            "seq_group": np.asarray(seq_group, np.int32),
+            "group_first": np.asarray([g[0] for g in groups], np.int32),
+            "group_size": np.asarray([g[1] for g in groups], np.int32),
+            "group_prefix": np.asarray([g[2] for g in groups], np.int32)}
+    return _assemble("shared_groups", dtype, num_q_heads, num_kv_heads, head_dim, B, num_blocks,
+                     1.0 / np.sqrt(d), ctx, tables, q, seq_tokens, alloc.refcount, meta)
+
+
+def shared_prefix_groups(case: PagedDecodeCase):
+    """The group arrays of a shared_prefix() batch: prompt p's samples are group p."""
+    samples, plen = case.meta["samples"], case.meta["prompt_len"]
+    ng = case.num_seqs // samples
+    return (np.arange(case.num_seqs, dtype=np.int32) // samples,
+            np.arange(ng, dtype=np.int32) * samples, np.full(ng, samples, np.int32),
+            np.full(ng, plen, np.int32))
 
 
 def long_context(block_size=16, variant="plain", num_seqs=8, lo=32768, hi=131072) -> PagedDecodeCase:
