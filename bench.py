@@ -70,11 +70,13 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="decode workloads: replay one captured HIP graph of the step instead of "
                          "launching every timed step from the host (slower on ROCm 7)")
-    ap.add_argument("--step", choices=["auto", "fused", "unfused"], default="auto",
+    ap.add_argument("--step", choices=["auto", "fused", "unfused", "shared"], default="auto",
                     help="decode workloads: 'fused' = one pa_decode_append (pa_decode_fp8_append) "
-                         "per step; 'unfused' = pa_cache_write(_fp8), then pa_decode(_fp8); 'auto' = "
-                         "fused for fp16 pools and unfused for E4M3 (and fp32) pools, the faster "
-                         "form of each on MI355X")
+                         "per step; 'unfused' = pa_cache_write(_fp8), then pa_decode(_fp8); "
+                         "'shared' (shared_prefix, fp16) = pa_cache_write, then pa_decode_shared, "
+                         "which streams each prompt's shared blocks once for all its samples; "
+                         "'auto' = shared for shared_prefix, fused for other fp16 pools and unfused "
+                         "for E4M3 (and fp32) pools, the faster form of each on MI355X")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic that scales the HBM byte counters)")
@@ -270,7 +272,9 @@ def run_one(args, config):
     # the slot its table gives position ctx - 1 (the workloads put it exactly there) and
     # attends.  By default for fp16 pools only: for E4M3 pools the fused stream kernel's
     # operand substitution costs as much as the separate store launch saves.
-    fused = case.dtype == np.float16 and (args.step == "fused" or (args.step == "auto" and not fp8))
+    shared = config == "shared_prefix" and not fp8 and case.dtype == np.float16 and \
+        args.step in ("auto", "shared")
+    fused = not shared and case.dtype == np.float16 and (args.step == "fused" or (args.step == "auto" and not fp8))
     if fused:
         last = case.context_lens.astype(np.int64) - 1
         table_slots = case.block_tables[np.arange(case.num_seqs), last // case.block_size].astype(np.int64) * \
@@ -279,6 +283,11 @@ def run_one(args, config):
 
     ws_bytes = P.pa_decode_workspace_bytes(case.num_seqs, case.num_q_heads, case.num_kv_heads,
                                            case.head_dim, mcl, partition)
+    if shared:
+        import workloads as W
+        groups = [t(a) for a in W.shared_prefix_groups(case)]
+        ws_bytes = P.pa_decode_shared_workspace_bytes(case.num_seqs, int(groups[1].shape[0]), case.num_q_heads,
+                                                      case.num_kv_heads, case.head_dim)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
@@ -299,7 +308,10 @@ def run_one(args, config):
             P.pa_cache_write(new_k, new_v, new_slots, k_cache, v_cache, stream=cur[0])
 
     def decode_only():
-        if fused and fp8:
+        if shared:
+            P.pa_decode_shared(out, q, k_cache, v_cache, tables, ctx, *groups, case.scale, case.block_size,
+                               case.num_kv_heads, max_context_len=mcl, workspace=ws, stream=cur[0])
+        elif fused and fp8:
             P.pa_decode_fp8_append(out, q, new_k, new_v, k_cache, v_cache, tables, ctx, case.scale,
                                    k_scale, v_scale, case.block_size, case.num_kv_heads,
                                    max_context_len=mcl, partition_size=partition, workspace=ws,
@@ -323,7 +335,11 @@ def run_one(args, config):
         decode_only()
 
     def stream_kernel():  # the first of the step's two attention launches, on its own
-        if fused and fp8:
+        if shared:
+            P.pa_decode_shared_partitions(out, q, k_cache, v_cache, tables, ctx, *groups, case.scale,
+                                          case.block_size, case.num_kv_heads, max_context_len=mcl,
+                                          workspace=ws, stream=stream)
+        elif fused and fp8:
             P.pa_decode_fp8_append_partitions(out, q, new_k, new_v, k_cache, v_cache, tables, ctx,
                                               case.scale, k_scale, v_scale, case.block_size,
                                               case.num_kv_heads, max_context_len=mcl,
@@ -429,13 +445,15 @@ def run_one(args, config):
     q_bytes = case.num_seqs * case.num_q_heads * case.head_dim * case.elt_bytes
     # K/V rows, q in, out, the table entries in use and the context lengths
     alg_bytes = kv_bytes + 2 * q_bytes + tokens_blocks * 4 + case.num_seqs * 4
+    unique = case.unique_kv_bytes() if config == "shared_prefix" else kv_bytes
+    if shared:  # the shared kernel reads each shared block once: its bytes are the unique ones
+        alg_bytes = alg_bytes - kv_bytes + unique
     kern_ms = primary_ms("kernel")
     achieved = alg_bytes / (kern_ms * 1e-3) / 1e9
     warm_achieved = alg_bytes / (timing["kernel"]["warm"] * 1e-3) / 1e9
     step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    kernel = stream_kernel_name(case.dtype == np.float16)
+    kernel = "pa_shared_mfma_kernel" if shared else stream_kernel_name(case.dtype == np.float16)
     traffic = measured_traffic(kernel, config, partition)
-    unique = case.unique_kv_bytes() if config == "shared_prefix" else kv_bytes
     # fp16 (or fp32) rows in, stored rows out
     write_bytes = 2 * case.num_seqs * case.num_kv_heads * case.head_dim * (case.elt_bytes + elt)
     dec_ms, wr_ms = primary_ms("decode"), primary_ms("write")
@@ -463,14 +481,19 @@ def run_one(args, config):
                             f"sum {int(case.context_lens.sum())}",
             "partition_size": partition, "kv_bytes_per_step": kv_bytes,
             "kv_cache": "e4m3" if fp8 else ("f16" if case.dtype == np.float16 else "f32"),
-            "step": ("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else
-                    "pa_cache_write + pa_decode",
+            "step": "pa_cache_write + pa_decode_shared" if shared else
+                    (("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else
+                     "pa_cache_write + pa_decode"),
             "graph": graph is not None,  # timed steps are replays of one captured HIP graph
+            **({"kv_bytes_counted": "every sequence's whole context, a shared prefix once per member; "
+                                    "pa_decode.unique_* and roofline count the distinct blocks"}
+               if unique != kv_bytes else {}),
         },
         "pct_hbm_peak": round(100.0 * step_gbs / HBM_PEAK_GBS, 2),
         "seqs_per_s_per_layer": round(case.num_seqs / (ms_per_step * 1e-3), 1),
         "pa_decode": {  # the whole call (both launches); figures from the cold median
-            "call": ("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else "pa_decode",
+            "call": "pa_decode_shared" if shared else
+                    (("pa_decode_fp8_append" if fp8 else "pa_decode_append") if fused else "pa_decode"),
             "us": round(dec_ms * 1e3, 2),
             **summary("decode"),
             "kv_gbs": round(gbs(kv_bytes, dec_ms), 1),
@@ -504,7 +527,7 @@ def run_one(args, config):
             "warm_frac": round(warm_achieved / HBM_PEAK_GBS, 4),
         },
     }
-    if unique != kv_bytes:  # shared blocks: the bytes HBM must deliver are the unique ones
+    if unique != kv_bytes and not shared:  # shared blocks: the bytes HBM must deliver are the unique ones
         alg_unique = alg_bytes - kv_bytes + unique
         result["roofline"]["unique_alg_bytes_per_launch"] = alg_unique
         result["roofline"]["unique_achieved"] = round(gbs(alg_unique, kern_ms), 1)

@@ -28,7 +28,8 @@ def test_header_declares_the_calls():
                  "pa_decode_partitions", "pa_decode_reduce", "pa_last_error", "pa_abi_version",
                  "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_fp8_partitions",
                  "pa_prefill", "pa_decode_append", "pa_decode_append_partitions",
-                 "pa_decode_fp8_append", "pa_decode_fp8_append_partitions"):
+                 "pa_decode_fp8_append", "pa_decode_fp8_append_partitions", "pa_decode_noalloc",
+                 "pa_decode_shared", "pa_decode_shared_partitions", "pa_decode_shared_workspace_bytes"):
         assert want in names
 
 
@@ -142,6 +143,65 @@ def test_decode_noalloc_rejects_bad_arguments(over, code):
 
 def test_decode_noalloc_with_no_sequences_is_a_no_op():
     assert _noalloc(S=0, out=None, q=None) == _lib.PA_OK
+    assert P.last_error() == ""
+
+
+def test_shared_workspace_size_query():
+    # per virtual segment (each group's prefix and each sequence's own part, per kv head) a
+    # 2-int descriptor and a record; besides, two records per wave of the 4096-wave cap; every
+    # record holds fp32 max and sum of 32 rows and 32 * head_dim fp32 outputs
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+
+    def layout(S, NG, hkv, d):
+        segs = (S + NG) * hkv
+        recs = 2 * 4096 + segs
+        return al(segs * 8) + 2 * al(recs * 32 * 4) + al(recs * 32 * d * 4)
+
+    assert P.pa_decode_shared_workspace_bytes(256, 16, 32, 8, 128) == layout(256, 16, 8, 128)
+    assert P.pa_decode_shared_workspace_bytes(3, 0, 8, 2, 64) == layout(3, 0, 2, 64)
+    assert P.pa_decode_shared_workspace_bytes(0, 1, 8, 2, 64) == 0
+    assert P.pa_decode_shared_workspace_bytes(4, -1, 8, 2, 64) == 0
+    assert P.pa_decode_shared_workspace_bytes(4, 1, 30, 8, 128) == 0  # 30 % 8 != 0
+
+
+def _shared(fn="pa_decode_shared", **over):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, ctx=FAKE, sg=FAKE, gf=FAKE, gs=FAKE, gp=FAKE, NG=2,
+             scale=1.0, B=16, hkv=8, S=4, hq=32, D=128, mb=16, mcl=256, N=100, ws=FAKE, wsb=1 << 30,
+             stream=None)
+    a.update(over)
+    return getattr(P.lib(), fn)(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["ctx"], a["sg"], a["gf"],
+                                a["gs"], a["gp"], a["NG"], a["scale"], a["B"], a["hkv"], a["S"], a["hq"],
+                                a["D"], a["mb"], a["mcl"], a["N"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("fn", ["pa_decode_shared", "pa_decode_shared_partitions"])
+@pytest.mark.parametrize("over,code", [
+    (dict(D=96), _lib.PA_ERR_UNSUPPORTED),
+    (dict(B=64), _lib.PA_ERR_UNSUPPORTED),
+    (dict(hq=8 * 17), _lib.PA_ERR_UNSUPPORTED),      # more than 16 query heads per kv head
+    (dict(hq=30), _lib.PA_ERR_INVALID_ARG),
+    (dict(mcl=257), _lib.PA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.PA_ERR_INVALID_ARG),
+    (dict(S=65536), _lib.PA_ERR_INVALID_ARG),
+    (dict(NG=-1), _lib.PA_ERR_INVALID_ARG),
+    (dict(NG=65536), _lib.PA_ERR_INVALID_ARG),
+    (dict(sg=None), _lib.PA_ERR_INVALID_ARG),
+    (dict(gp=None), _lib.PA_ERR_INVALID_ARG),        # NULL group arrays with groups
+    (dict(gf=FAKE + 2), _lib.PA_ERR_INVALID_ARG),    # misaligned
+    (dict(q=FAKE + 8), _lib.PA_ERR_INVALID_ARG),
+    (dict(ws=None), _lib.PA_ERR_WORKSPACE),
+    (dict(wsb=1024), _lib.PA_ERR_WORKSPACE),
+    (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),
+    # more than 2^31 - 1 tiles over the virtual segments, though the sequences alone fit
+    (dict(S=65535, NG=65535, hkv=2, hq=2, mb=8192, mcl=131072, wsb=1 << 50), _lib.PA_ERR_INVALID_ARG),
+])
+def test_decode_shared_rejects_bad_arguments(fn, over, code):
+    assert _shared(fn, **over) == code
+    assert P.last_error() != ""
+
+
+def test_decode_shared_with_no_sequences_is_a_no_op():
+    assert _shared(S=0, out=None, q=None, ws=None) == _lib.PA_OK
     assert P.last_error() == ""
 
 
