@@ -1903,26 +1903,52 @@ struct VCursor {
   int pos0;    // position of its first token in that row
   int s0;      // sequence of its first query row
   int rows;    // query rows per kv head (members x group, or group)
+  int wt;      // cost of one of its tiles
+  int c0;      // cost position where the segment starts
 };
+
+// The work split.  Waves take equal shares of an estimated cost, not of tiles: a tile of
+// one 16-row block costs kShTileCost, one of two blocks kShTileCost2, and each segment
+// kShSegCost besides (its start and end: q rows, records, cursor), in units of about
+// 0.2 us measured on MI355X.  With equal tile shares, the waves that took many short own
+// parts finished last, a piece boundary costing about as much as a tile.  Segment k starts
+// at cost position c0 and its tile t sits at c0 + kShSegCost + t wt; wave w takes the tiles
+// at positions p with floor(p Wp / total) = w, a contiguous range.  Wp = min(waves,
+// total / kShTileCost2), so that every share is at least one tile's cost wide: no wave
+// inside a segment's span is left without a tile of it, as the reduce's records require.
+constexpr int kShTileCost = 4, kShTileCost2 = 5, kShSegCost = 6;
 
 template <int TK>
 struct VWork {
+  static constexpr int kChunks = 4;  // chunks of 64 virtual sequences the scans keep per lane
   const int32_t* ctxs;
   SharedArgs sh;
   int S, NG, V, max_ctx, n_units, G, bsz;
-  int Q, R, A, n_my;
+  int Wp;         // waves sharing the work
+  int total;      // total cost (the host bounds it below 2^31)
+  double inv_total;
+  int A, n_my;
+
+  // floor(n / d) for 0 <= n < 2^53 and 0 < d < 2^31: a double estimate (off by at most one
+  // for these sizes), corrected with exact integer products
+  __device__ static int64_t div_floor(int64_t n, int64_t d, double inv_d) {
+    int64_t q = static_cast<int64_t>(static_cast<double>(n) * inv_d);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+  }
 
   __device__ static int tiles(int c) { return c > 0 ? (c + TK - 1) / TK : 0; }
+  __device__ static int tile_cost(int rows) { return rows > kMfRows ? kShTileCost2 : kShTileCost; }
 
   // Virtual sequence v: its tokens, table row, first position, first query sequence and
-  // query rows per kv head.  LOAD reads one 32-bit element (vector loads for the
-  // lane-parallel scans, scalar loads for the cursor).  Tokens are 0 (nothing streamed)
-  // for an invalid group, a prefix of no valid group, or an own part that is invalid; the
-  // reduce gives the affected rows NaN.
-  template <typename Load>
-  __device__ void geom(int v, Load load, int& ctxv, int& trow, int& pos0, int& s0, int& rows) const {
+  // query rows per kv head, read with scalar loads.  Tokens are 0 (nothing streamed) for an
+  // invalid group, a prefix of no valid group, or an own part that is invalid; the reduce
+  // gives the affected rows NaN.
+  __device__ void geom(int v, int& ctxv, int& trow, int& pos0, int& s0, int& rows) const {
     if (v < NG) {
-      const int L = load(sh.group_prefix + v), n = load(sh.group_size + v), f = load(sh.group_first + v);
+      const int L = scalar_load(sh.group_prefix + v), n = scalar_load(sh.group_size + v),
+                f = scalar_load(sh.group_first + v);
       const bool ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx);
       ctxv = ok ? L : 0;
       trow = ok ? f : 0;
@@ -1931,15 +1957,15 @@ struct VWork {
       rows = ok ? n * G : G;
     } else {
       const int s = v - NG;
-      const int c = load(ctxs + s);
-      const int gi = load(sh.seq_group + s);
+      const int c = scalar_load(ctxs + s);
+      const int gi = scalar_load(sh.seq_group + s);
       int L = 0;
       bool ok = c > 0 && c <= max_ctx;
       if (gi >= 0) {
         ok = ok && gi < NG;
         if (ok) {  // the group arrays are read only at valid indexes (they may be empty)
-          L = load(sh.group_prefix + gi);
-          const int n = load(sh.group_size + gi), f = load(sh.group_first + gi);
+          L = scalar_load(sh.group_prefix + gi);
+          const int n = scalar_load(sh.group_size + gi), f = scalar_load(sh.group_first + gi);
           ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx) && s >= f && s < f + n && L <= c;
         }
       }
@@ -1951,7 +1977,56 @@ struct VWork {
     }
   }
 
-  __device__ void init(const StreamArgs& a, const SharedArgs& shv, int w, int lane, int bs) {
+  // The same for the lanes' virtual sequences v (v >= V gives 0 tokens), as vector loads
+  // issued at clamped valid indexes whatever the lane's case, in two dependent rounds (the
+  // own part's group comes from its sequence), so that the loads of several chunks can be
+  // in flight together.  S > 0.
+  __device__ void geom_lanes1(int v, int& c, int& gi, int& Lp, int& np, int& fp) const {
+    const int s = min(max(v - NG, 0), S - 1);
+    c = ctxs[s];
+    gi = sh.seq_group[s];
+    Lp = np = fp = 0;
+    if (NG > 0) {
+      const int gv = min(v, NG - 1);
+      Lp = sh.group_prefix[gv];
+      np = sh.group_size[gv];
+      fp = sh.group_first[gv];
+    }
+  }
+  __device__ void geom_lanes2(int v, int c, int gi, int Lp, int np, int fp, int& ctxv, int& trow, int& pos0,
+                              int& s0, int& rows) const {
+    int Lo = 0, no = 0, fo = 0;
+    const bool has_g = v >= NG && gi >= 0 && gi < NG;
+    if (NG > 0) {
+      const int gc = has_g ? gi : 0;
+      Lo = sh.group_prefix[gc];
+      no = sh.group_size[gc];
+      fo = sh.group_first[gc];
+    }
+    if (v < NG) {
+      const bool ok = shared_group_ok(Lp, np, fp, S, G, bsz, max_ctx);
+      ctxv = ok ? Lp : 0;
+      trow = ok ? fp : 0;
+      pos0 = 0;
+      s0 = trow;
+      rows = ok ? np * G : G;
+    } else {
+      const int s = v - NG;
+      bool ok = c > 0 && c <= max_ctx;
+      if (gi >= 0)
+        ok = ok && has_g && shared_group_ok(Lo, no, fo, S, G, bsz, max_ctx) && s >= fo && s < fo + no && Lo <= c;
+      const int L = gi >= 0 ? Lo : 0;
+      ctxv = ok ? c - L : 0;
+      trow = s;
+      pos0 = ok ? L : 0;
+      s0 = s;
+      rows = G;
+    }
+    if (v >= V) ctxv = 0;
+  }
+
+  // Split the work and place cursor c at this wave's first tile (n_my = 0: nothing to do).
+  __device__ void init(const StreamArgs& a, const SharedArgs& shv, int w, int lane, int bs, VCursor& c) {
     ctxs = a.context_lens;
     sh = shv;
     S = a.num_seqs;
@@ -1961,61 +2036,135 @@ struct VWork {
     n_units = a.num_kv_heads;
     G = a.group;
     bsz = bs;
-    const auto vload = [](const int32_t* p) { return *p; };
-    int part = 0;
-    for (int b = 0; b < V; b += kWave) {
-      if (b + lane < V) {
-        int cv, tr, p0, s0, rw;
-        geom(b + lane, vload, cv, tr, p0, s0, rw);
-        part += tiles(cv);
-      }
+    n_my = 0;
+    A = 0;
+    const int nch = (V + kWave - 1) / kWave;
+    const bool cached = nch <= kChunks;
+    int k_ctx[kChunks], k_trow[kChunks], k_pos0[kChunks], k_s0[kChunks], k_rows[kChunks];
+    auto chunk = [&](int b, int& ctxv, int& trow, int& pos0, int& s0, int& rows) __attribute__((always_inline)) {
+      int cv, gi, Lp, np, fp;
+      geom_lanes1(b * kWave + lane, cv, gi, Lp, np, fp);
+      geom_lanes2(b * kWave + lane, cv, gi, Lp, np, fp, ctxv, trow, pos0, s0, rows);
+    };
+    if (cached) {  // both rounds of loads of all chunks at once
+      int cv[kChunks], gi[kChunks], Lp[kChunks], np[kChunks], fp[kChunks];
+#pragma unroll
+      for (int b = 0; b < kChunks; ++b)
+        if (b < nch) geom_lanes1(b * kWave + lane, cv[b], gi[b], Lp[b], np[b], fp[b]);
+#pragma unroll
+      for (int b = 0; b < kChunks; ++b)
+        if (b < nch)
+          geom_lanes2(b * kWave + lane, cv[b], gi[b], Lp[b], np[b], fp[b], k_ctx[b], k_trow[b], k_pos0[b], k_s0[b],
+                      k_rows[b]);
     }
-    const int total = wave_sum_int(part) * n_units;
-    Q = total / a.num_waves;
-    R = total - Q * a.num_waves;
-    A = w * Q + min(w, R);
-    n_my = Q + (w < R ? 1 : 0);
+    // totals
+    int part_tiles = 0, part_cost = 0;
+    for (int b = 0; b < nch; ++b) {
+      int ctxv, trow, pos0, s0, rows;
+      if (cached) {
+        ctxv = pick(k_ctx, b);
+        rows = pick(k_rows, b);
+      } else {
+        chunk(b, ctxv, trow, pos0, s0, rows);
+      }
+      const int nt = tiles(ctxv);
+      part_tiles += nt * n_units;
+      part_cost += nt > 0 ? n_units * (kShSegCost + nt * tile_cost(rows)) : 0;
+    }
+    const int T = wave_sum_int(part_tiles);
+    total = wave_sum_int(part_cost);
+    Wp = min(a.num_waves, total / kShTileCost2);
+    if (T == 0 || w >= Wp) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      return;
+    }
+    inv_total = 1.0 / static_cast<double>(total);
+    const double inv_wp = 1.0 / static_cast<double>(Wp);
+    const int th0 = static_cast<int>(div_floor(static_cast<int64_t>(w) * total + Wp - 1, Wp, inv_wp));
+    const int th1 =
+        w + 1 == Wp ? total : static_cast<int>(div_floor(static_cast<int64_t>(w + 1) * total + Wp - 1, Wp, inv_wp));
+    // the first tiles at positions >= th0 and >= th1
+    int x0 = -1, x1 = T;
+    int base_t = 0, base_c = 0;
+    for (int b = 0; b < nch && x1 == T; ++b) {
+      int ctxv, trow, pos0, s0, rows;
+      if (cached) {
+        ctxv = pick(k_ctx, b);
+        trow = pick(k_trow, b);
+        pos0 = pick(k_pos0, b);
+        s0 = pick(k_s0, b);
+        rows = pick(k_rows, b);
+      } else {
+        chunk(b, ctxv, trow, pos0, s0, rows);
+      }
+      const int nt = tiles(ctxv), wt = tile_cost(rows);
+      const int tl = nt * n_units, cost = nt > 0 ? n_units * (kShSegCost + nt * wt) : 0;
+      const int ti = wave_incl_scan_int(tl, lane), ci = wave_incl_scan_int(cost, lane);
+      const int Gv = base_t + ti - tl, Cv = base_c + ci - cost;
+      // v's last tile sits at Cv + cost - wt; the first v whose last tile reaches th holds it
+      auto find = [&](int th, int& x, bool cursor) __attribute__((always_inline)) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nt > 0 && Cv + cost - wt >= th);
+        if (hit == 0) return;
+        const int l = __builtin_ctzll(hit);
+        const int ntl = __builtin_amdgcn_readlane(nt, l), wtl = __builtin_amdgcn_readlane(wt, l);
+        const int Cl = __builtin_amdgcn_readlane(Cv, l), Gl = __builtin_amdgcn_readlane(Gv, l);
+        const int sz = kShSegCost + ntl * wtl;
+        const int rem = th - Cl - kShSegCost - (ntl - 1) * wtl;  // unit u's last tile reaches th
+        const int u = rem > 0 ? (rem + sz - 1) / sz : 0;
+        const int cs = Cl + u * sz;
+        const int rt = th - cs - kShSegCost;
+        const int t = rt > 0 ? (rt + wtl - 1) / wtl : 0;
+        x = Gl + u * ntl + t;
+        if (cursor) {
+          c.v = b * kWave + l;
+          c.unit = u;
+          c.t = t;
+          c.nt = ntl;
+          c.ctx = __builtin_amdgcn_readlane(ctxv, l);
+          c.gstart = Gl + u * ntl;
+          c.trow = __builtin_amdgcn_readlane(trow, l);
+          c.pos0 = __builtin_amdgcn_readlane(pos0, l);
+          c.s0 = __builtin_amdgcn_readlane(s0, l);
+          c.rows = __builtin_amdgcn_readlane(rows, l);
+          c.wt = wtl;
+          c.c0 = cs;
+        }
+      };
+      if (x0 < 0) find(th0, x0, true);
+      if (w + 1 < Wp) find(th1, x1, false);
+      base_t += __builtin_amdgcn_readlane(ti, kWave - 1);
+      base_c += __builtin_amdgcn_readlane(ci, kWave - 1);
+    }
+    A = x0;
+    n_my = x0 < 0 ? 0 : x1 - x0;
+    // every load of the scans is complete before the stream's first loads (without this the
+    // compiler may drain all of them, the stream's too, in front of the loop)
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
 
-  __device__ int wave_of(int x) const {
-    const int cut = R * (Q + 1);
-    return (x < cut || Q == 0) ? x / (Q + 1) : R + (x - cut) / Q;
+  __device__ static int pick(const int (&k)[kChunks], int b) {
+    int r = k[0];
+#pragma unroll
+    for (int i = 1; i < kChunks; ++i) r = b == i ? k[i] : r;
+    return r;
+  }
+
+  // the wave holding the last tile of c's segment
+  __device__ int wave_of_last(const VCursor& c) const {
+    const int p = c.c0 + kShSegCost + (c.nt - 1) * c.wt;
+    return static_cast<int>(div_floor(static_cast<int64_t>(p) * Wp, total, inv_total));
   }
 
   __device__ void set(VCursor& c, int v) const {
     c.v = v;
-    geom(v, [](const int32_t* p) { return scalar_load(p); }, c.ctx, c.trow, c.pos0, c.s0, c.rows);
+    geom(v, c.ctx, c.trow, c.pos0, c.s0, c.rows);
     c.nt = tiles(c.ctx);
-  }
-
-  // cursor at global tile x (below the total)
-  __device__ VCursor locate(int x, int lane) const {
-    const auto vload = [](const int32_t* p) { return *p; };
-    int v0 = 0, base = 0;
-    for (int b = 0; b < V; b += kWave) {
-      int cv = 0, tr, p0, s0, rw;
-      if (b + lane < V) geom(b + lane, vload, cv, tr, p0, s0, rw);
-      const int ts = tiles(cv) * n_units;
-      const int incl = wave_incl_scan_int(ts, lane);
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > x);
-      if (hit != 0) {
-        const int l = __builtin_ctzll(hit);
-        v0 = b + l;
-        base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
-        break;
-      }
-      base += __builtin_amdgcn_readlane(incl, kWave - 1);
-    }
-    VCursor c;
-    set(c, v0);
-    c.unit = (x - base) / c.nt;
-    c.t = (x - base) - c.unit * c.nt;
-    c.gstart = base + c.unit * c.nt;
-    return c;
+    c.wt = tile_cost(c.rows);
   }
 
   __device__ void advance(VCursor& c) const {
     if (++c.t < c.nt) return;
+    c.c0 += kShSegCost + c.nt * c.wt;
     c.gstart += c.nt;
     c.t = 0;
     if (++c.unit < n_units) return;
@@ -2058,11 +2207,11 @@ __global__ __launch_bounds__(kWave) void pa_shared_mfma_kernel(const StreamArgs 
   const int bsz = a.block_size;
 
   VWork<TK> wk;
-  wk.init(a, sh, w, lane, bsz);
+  VCursor cc;
+  wk.init(a, sh, w, lane, bsz, cc);
   const int n_my = wk.n_my;
   if (n_my == 0) return;
   const int A = wk.A, A_end = A + n_my;
-  VCursor cc = wk.locate(A, lane);
 
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
   uint32_t ka[KB], va[NB];
@@ -2184,7 +2333,7 @@ __global__ __launch_bounds__(kWave) void pa_shared_mfma_kernel(const StreamArgs 
     });
     piece_bad = false;
     if (cc.t == 0 && lane == 0)
-      a.seg_desc[cc.v * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+      a.seg_desc[cc.v * a.n_units + cc.unit] = make_int2(w, wk.wave_of_last(cc));
   };
 
   auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
@@ -3519,6 +3668,11 @@ int decode_shared(int launches, void* out, const void* q, const void* k_cache, c
           std::max<int64_t>(1, (static_cast<int64_t>(max_context_len) + 7) / 8) >
       (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
+  // the work split's cost positions are 32-bit
+  if ((static_cast<int64_t>(num_seqs) + num_groups) * num_kv_heads *
+          (kShSegCost + kShTileCost2 * ((static_cast<int64_t>(max_context_len) + 15) / 16)) >
+      (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large for the shared-prefix work split");
   if (num_seqs == 0) return PA_OK;
   if (!seq_group || (num_groups > 0 && (!group_first || !group_size || !group_prefix)))
     return fail(PA_ERR_INVALID_ARG, "a group array is NULL");

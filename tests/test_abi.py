@@ -194,6 +194,8 @@ def _shared(fn="pa_decode_shared", **over):
     (dict(ws=FAKE + 16), _lib.PA_ERR_WORKSPACE),
     # more than 2^31 - 1 tiles over the virtual segments, though the sequences alone fit
     (dict(S=65535, NG=65535, hkv=2, hq=2, mb=8192, mcl=131072, wsb=1 << 50), _lib.PA_ERR_INVALID_ARG),
+    # within the tile bound, but the work split's 32-bit cost positions would overflow
+    (dict(S=8192, NG=0, hkv=8, hq=32, mb=8192, mcl=131072, wsb=1 << 50), _lib.PA_ERR_INVALID_ARG),
 ])
 def test_decode_shared_rejects_bad_arguments(fn, over, code):
     assert _shared(fn, **over) == code
