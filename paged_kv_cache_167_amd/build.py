@@ -28,6 +28,10 @@ def command(out: str = LIB) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed-FP32 VALU forms are kept out of every kernel
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix products accumulate in ordinary vector registers: every kernel fits in them,
+        # and accumulators kept in the accumulation registers were copied to vector registers
+        # and back on each tile wherever vector instructions also touch them (the rescale)
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", "-o", out, *SOURCES,
     ]

@@ -2352,16 +2352,27 @@ __global__ __launch_bounds__(kWave) void pa_shared_mfma_kernel(const StreamArgs 
         vop[nb] = __builtin_bit_cast(f16x4, x);
       }
     }
+    // the score products of every row block first, then each block's softmax and P.V: the
+    // second block's products run while the first block's softmax does, and the first
+    // block's P.V while the second block's softmax does (matrix and vector instructions of
+    // one wave execute together)
+    const bool two = rows > 16;  // wave-uniform
+    f32x4 scs[NRB];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      if (rb > 0 && rows <= 16) break;  // wave-uniform: one row block
+      if (rb > 0 && !two) break;
       f32x4 sa = {0.0f, 0.0f, 0.0f, 0.0f}, sb = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if (kb & 1) sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[rb][kb], sb, 0, 0, 0);
         else sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[kb], qop[rb][kb], sa, 0, 0, 0);
       }
-      const f32x4 sc = sa + sb;
+      scs[rb] = sa + sb;
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (rb > 0 && !two) break;  // wave-uniform: one row block
+      const f32x4 sc = scs[rb];
       float mt = -INFINITY;
 #pragma unroll
       for (int i = 0; i < 4; ++i) mt = fmaxf(mt, ok[i] ? sc[i] : -INFINITY);
