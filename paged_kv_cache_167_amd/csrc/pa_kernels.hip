@@ -465,77 +465,119 @@ struct Cursor {
   int nt;      // tiles in the segment
   int ctx;     // context length of the sequence
   int gstart;  // global index of the segment's first tile
+  int seg;     // non-empty segments before this one
 };
 
-// The batch as one list of tiles (TK consecutive tokens of one segment, segments in
-// order), and one wave's equal share of it.  Every member is wave-uniform.
+// The work split.  The batch is one list of tiles (TK consecutive tokens of one segment,
+// segments in order), and each wave takes an equal share of an estimated cost: a tile
+// costs one unit, and each non-empty segment one more (a piece boundary -- q rows, record,
+// cursor -- costs about as much as a tile on MI355X), so that a wave whose share crosses
+// more boundaries takes fewer tiles.  Tile x of a segment with j non-empty segments before
+// it sits at cost position x + j + 1; wave w takes the tiles at positions p with
+// floor(p Wp / total) = w, a contiguous range.  Wp = min(waves, total): every share is at
+// least one position wide, so no wave inside a segment's span is left without a tile of it
+// (the reduce takes one piece from each wave of a segment's {first, last} range).
 template <int TK>
 struct Work {
   const int32_t* ctxs;
   int S, max_ctx, n_units;
-  int Q, R;     // every wave takes Q tiles, the first R waves one more
-  int A, n_my;  // this wave's share: tiles [A, A + n_my)
-  int ctx0;     // this lane's context length among the first 64 sequences (0 past S): one
-                // load serves the total, the scan and the cursor
+  int Wp;           // waves sharing the work
+  int total;        // tiles plus non-empty segments (the host bounds it below 2^31)
+  double inv_total;
+  int A, n_my;      // this wave's share: tiles [A, A + n_my)
+  int ctx0;         // this lane's context length among the first 64 sequences (0 past S): one
+                    // load serves the totals and the scan
 
   __device__ int seg_tiles(int ctx) const {  // invalid or empty contexts contribute no tiles
     return (ctx > 0 && ctx <= max_ctx) ? (ctx + TK - 1) / TK : 0;
   }
 
-  __device__ void init(const StreamArgs& a, int w, int lane) {
+  // floor(n / d) for 0 <= n < 2^53 and 0 < d < 2^31: a double estimate (off by at most one
+  // for these sizes), corrected with exact integer products
+  __device__ static int64_t div_floor(int64_t n, int64_t d, double inv_d) {
+    int64_t q = static_cast<int64_t>(static_cast<double>(n) * inv_d);
+    if (q * d > n) --q;
+    else if ((q + 1) * d <= n) ++q;
+    return q;
+  }
+
+  // Split the work and place cursor c at this wave's first tile (n_my = 0: nothing to do).
+  __device__ void init(const StreamArgs& a, int w, int lane, Cursor& c) {
     ctxs = a.context_lens;
     S = a.num_seqs;
     max_ctx = a.max_context_len;
     n_units = a.n_units;
+    n_my = 0;
+    A = 0;
     ctx0 = lane < S ? ctxs[lane] : 0;
-    int part = seg_tiles(ctx0);
-    for (int b = kWave; b < S; b += kWave) part += (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
-    const int total = wave_sum_int(part) * n_units;
-    Q = total / a.num_waves;
-    R = total - Q * a.num_waves;
-    A = w * Q + min(w, R);
-    n_my = Q + (w < R ? 1 : 0);
-  }
-
-  __device__ int wave_of(int x) const {  // the wave whose share holds global tile x
-    const int cut = R * (Q + 1);
-    return (x < cut || Q == 0) ? x / (Q + 1) : R + (x - cut) / Q;
-  }
-
-  // Cursor at tile A: scan the per-sequence tile counts for the sequence covering it.
-  __device__ Cursor locate(int lane) const {
-    int s0 = 0, base = 0;  // base: global index of s0's first tile
-    int cx = 0;            // context length of s0
-    bool found = false;
-    for (int b = 0; b < S; b += kWave) {
-      const int cl = b == 0 ? ctx0 : ((b + lane < S) ? ctxs[b + lane] : 0);
-      const int ts = seg_tiles(cl) * n_units;
-      const int incl = wave_incl_scan_int(ts, lane);
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > A);
-      if (hit != 0) {
-        const int l = __builtin_ctzll(hit);
-        s0 = b + l;
-        cx = __builtin_amdgcn_readlane(cl, l);
-        found = true;
-        base += __builtin_amdgcn_readlane(incl, l) - __builtin_amdgcn_readlane(ts, l);
-        break;
-      }
-      base += __builtin_amdgcn_readlane(incl, kWave - 1);
+    int part = seg_tiles(ctx0), nseg = part > 0 ? 1 : 0;
+    for (int b = kWave; b < S; b += kWave) {
+      const int nt = (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
+      part += nt;
+      nseg += nt > 0 ? 1 : 0;
     }
-    Cursor c;
-    c.s = s0;
-    c.ctx = found ? cx : scalar_load(ctxs + s0);
-    c.nt = seg_tiles(c.ctx);
-    c.unit = (A - base) / c.nt;
-    c.t = (A - base) - c.unit * c.nt;
-    c.gstart = base + c.unit * c.nt;
-    return c;
+    const int T = wave_sum_int(part) * n_units;
+    total = T + wave_sum_int(nseg) * n_units;
+    Wp = min(a.num_waves, total);
+    if (T == 0 || w >= Wp) return;
+    inv_total = 1.0 / static_cast<double>(total);
+    const double inv_wp = 1.0 / static_cast<double>(Wp);
+    const int th0 = static_cast<int>(div_floor(static_cast<int64_t>(w) * total + Wp - 1, Wp, inv_wp));
+    const int th1 =
+        w + 1 == Wp ? total : static_cast<int>(div_floor(static_cast<int64_t>(w + 1) * total + Wp - 1, Wp, inv_wp));
+    // the first tiles at positions >= th0 and >= th1 (th1 = total: none, the end)
+    int x0 = -1, x1 = T;
+    int base_t = 0, base_j = 0;  // tiles and non-empty segments before the chunk
+    for (int b = 0; b < S && x1 == T; b += kWave) {
+      const int cl = b == 0 ? ctx0 : ((b + lane < S) ? ctxs[b + lane] : 0);
+      const int nt = seg_tiles(cl);
+      const int ts = nt * n_units, ss = nt > 0 ? n_units : 0;
+      const int ti = wave_incl_scan_int(ts, lane), si = wave_incl_scan_int(ss, lane);
+      const int Gs = base_t + ti - ts, Js = base_j + si - ss;
+      // the sequence's last tile sits at Gs + ts - 1 + Js + ss; the first sequence whose last
+      // tile reaches th holds the first tile at or past th
+      auto find = [&](int th, int& x, bool cursor) __attribute__((always_inline)) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nt > 0 && Gs + ts + Js + ss - 1 >= th);
+        if (hit == 0) return;
+        const int l = __builtin_ctzll(hit);
+        const int ntl = __builtin_amdgcn_readlane(nt, l);
+        const int gj = __builtin_amdgcn_readlane(Gs, l) + __builtin_amdgcn_readlane(Js, l);
+        // unit u's last tile sits at gj + (u + 1)(nt + 1) - 1
+        const int ru = th - gj + 1;
+        const int u = ru > 0 ? max(0, (ru + ntl) / (ntl + 1) - 1) : 0;
+        const int rt = th - gj - u * (ntl + 1) - 1;  // tile t sits at gj + u (nt + 1) + t + 1
+        const int t = rt > 0 ? rt : 0;
+        x = __builtin_amdgcn_readlane(Gs, l) + u * ntl + t;
+        if (cursor) {
+          c.s = b + l;
+          c.ctx = __builtin_amdgcn_readlane(cl, l);
+          c.nt = ntl;
+          c.unit = u;
+          c.t = t;
+          c.gstart = __builtin_amdgcn_readlane(Gs, l) + u * ntl;
+          c.seg = __builtin_amdgcn_readlane(Js, l) + u;
+        }
+      };
+      if (x0 < 0) find(th0, x0, true);
+      if (w + 1 < Wp) find(th1, x1, false);
+      base_t += __builtin_amdgcn_readlane(ti, kWave - 1);
+      base_j += __builtin_amdgcn_readlane(si, kWave - 1);
+    }
+    A = x0;
+    n_my = x0 < 0 ? 0 : x1 - x0;
+  }
+
+  // the wave holding the last tile of c's segment
+  __device__ int wave_of_last(const Cursor& c) const {
+    const int p = c.gstart + c.nt - 1 + c.seg + 1;
+    return static_cast<int>(div_floor(static_cast<int64_t>(p) * Wp, total, inv_total));
   }
 
   __device__ void advance(Cursor& c) const {
     if (++c.t < c.nt) return;
     c.gstart += c.nt;
     c.t = 0;
+    ++c.seg;
     if (++c.unit < n_units) return;
     c.unit = 0;
     do {
@@ -674,11 +716,11 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
 
   // ---- this wave's share of the batch's tiles, and the cursor at its first tile
   Work<TK> wk;
-  wk.init(a, w, lane);
+  Cursor cc;  // the tile being computed
+  wk.init(a, w, lane, cc);
   const int n_my = wk.n_my;
   if (n_my == 0) return;
   const int A = wk.A, A_end = A + n_my;
-  Cursor cc = wk.locate(lane);  // the tile being computed
   auto advance = [&](Cursor& c) { wk.advance(c); };
 
   // ---- direct-to-LDS loads of one tile into a ring stage
@@ -767,7 +809,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     }
     piece_bad = false;
     if (cc.t == 0 && lane == 0)  // this wave starts the segment: record who holds its pieces
-      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of_last(cc));
     // Wait for the q rows here, once per piece.  Left to the compiler, the wait lands at
     // the first use of q on every tile (it cannot tell whether this branch ran) and would
     // drain the K/V loads in flight each time.
@@ -1417,11 +1459,11 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   const int jq = lane / 16;  // token quarter: tokens 4 jq .. 4 jq + 3 of a tile
 
   Work<TK> wk;
-  wk.init(a, w, lane);
+  Cursor cc;
+  wk.init(a, w, lane, cc);
   const int n_my = wk.n_my;
   if (n_my == 0) return;
   const int A = wk.A, A_end = A + n_my;
-  Cursor cc = wk.locate(lane);
 
   // ---- per-lane LDS addresses (within a stage) of the operands, and of the loads
   const uint32_t ring = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_ring));
@@ -1625,7 +1667,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     l = 0.0f;
     piece_bad = false;
     if (cc.t == 0 && lane == 0)
-      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of(cc.gstart + cc.nt - 1));
+      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of_last(cc));
   };
 
   auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
@@ -3222,10 +3264,10 @@ int check_decode(const DecodeCall& c, Geom* g, bool need_ws = true) {
   if (c.num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", c.num_q_heads);
   *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size,
                 c.dtype);
-  // tile counts and segment indexes are 32-bit in the kernels (a tile holds at least 8
-  // tokens; every segment counts as at least one tile, since the reduce indexes all of them)
-  if (static_cast<int64_t>(c.num_seqs) * g->n_units *
-          std::max<int64_t>(1, (static_cast<int64_t>(c.max_context_len) + 7) / 8) >
+  // tile counts, segment indexes and the work split's cost positions (tiles plus segments)
+  // are 32-bit in the kernels (a tile holds at least 8 tokens; every segment counts once
+  // besides, since the split and the reduce count all of them)
+  if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8 + 1) >
       (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
   if (c.num_blocks > (static_cast<int64_t>(1) << 31) - 1)

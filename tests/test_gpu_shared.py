@@ -107,6 +107,24 @@ def test_shared_small(D, B, hq, hkv, li):
     _fp16_bound(got, plain.astype(np.float64), case, f"{label} vs pa_decode")
 
 
+@pytest.mark.parametrize("D,B", [(128, 16), (64, 16), (128, 8)])
+def test_shared_short_prefixes_of_two_row_blocks(D, B):
+    """Groups of 8 members x 4 query heads (32 rows, two 16-row blocks) whose prefixes span one
+    or two tiles: their segments start a tile or two apart, so the second block's rows of some
+    must be read without the one extra LDS buffer the kernel keeps for them."""
+    layout = [("g", 16, [0, 1, 2, 3, 4, 5, 6, 7]), ("g", 32, [1, 9, 0, 2, 17, 5, 3, 1]), ("s", 7),
+              ("g", 16, [3, 3, 3, 3, 3, 3, 3, 3]), ("g", 48, [0, 40, 2, 2, 2, 2, 2, 80])]
+    label = f"short 32-row prefixes D{D} B{B}"
+    G.say(label)
+    case = W.shared_groups(layout, seed=15 + D + B, num_q_heads=32, num_kv_heads=8, head_dim=D, block_size=B)
+    d = G.to_device(case)
+    got = _shared(case, d, _groups(case))
+    kc, vc = oracle_pools(case)
+    ref = oracle_decode(case, kc, vc)
+    G.assert_close(got, ref, np.float16, label)
+    _fp16_bound(got, ref, case, label)
+
+
 def test_shared_repeatable_bitwise():
     case = W.shared_groups(LAYOUTS[1], seed=7)
     d = G.to_device(case)
