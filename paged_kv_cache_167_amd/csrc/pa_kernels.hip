@@ -1984,13 +1984,22 @@ struct VWork {
   __device__ static int tile_cost(int rows) { return rows > kMfRows ? kShTileCost2 : kShTileCost; }
 
   // Virtual sequence v: its tokens, table row, first position, first query sequence and
-  // query rows per kv head, read with scalar loads.  Tokens are 0 (nothing streamed) for an
-  // invalid group, a prefix of no valid group, or an own part that is invalid; the reduce
-  // gives the affected rows NaN.
+  // query rows per kv head, read with scalar loads (batched: one wait for a prefix, two for
+  // an own part).  Tokens are 0 (nothing streamed) for an invalid group, a prefix of no
+  // valid group, or an own part that is invalid; the reduce gives the affected rows NaN.
   __device__ void geom(int v, int& ctxv, int& trow, int& pos0, int& s0, int& rows) const {
+    // the group's prefix, size and first member (read twice: a batch of four)
+    auto group = [&](int gi, int& L, int& n, int& f) __attribute__((always_inline)) {
+      int32_t p[4];
+      load_entries4(uniform_ptr(sh.group_prefix + gi), uniform_ptr(sh.group_size + gi),
+                    uniform_ptr(sh.group_first + gi), uniform_ptr(sh.group_first + gi), p);
+      L = p[0];
+      n = p[1];
+      f = p[2];
+    };
     if (v < NG) {
-      const int L = scalar_load(sh.group_prefix + v), n = scalar_load(sh.group_size + v),
-                f = scalar_load(sh.group_first + v);
+      int L, n, f;
+      group(v, L, n, f);
       const bool ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx);
       ctxv = ok ? L : 0;
       trow = ok ? f : 0;
@@ -1999,15 +2008,16 @@ struct VWork {
       rows = ok ? n * G : G;
     } else {
       const int s = v - NG;
-      const int c = scalar_load(ctxs + s);
-      const int gi = scalar_load(sh.seq_group + s);
+      int32_t q[2];
+      load_entries2(uniform_ptr(ctxs + s), uniform_ptr(sh.seq_group + s), q);
+      const int c = q[0], gi = q[1];
       int L = 0;
       bool ok = c > 0 && c <= max_ctx;
       if (gi >= 0) {
         ok = ok && gi < NG;
         if (ok) {  // the group arrays are read only at valid indexes (they may be empty)
-          L = scalar_load(sh.group_prefix + gi);
-          const int n = scalar_load(sh.group_size + gi), f = scalar_load(sh.group_first + gi);
+          int n, f;
+          group(gi, L, n, f);
           ok = shared_group_ok(L, n, f, S, G, bsz, max_ctx) && s >= f && s < f + n && L <= c;
         }
       }
@@ -2552,16 +2562,22 @@ __global__ __launch_bounds__(kWave) void pa_shared_reduce_kernel(f16* __restrict
   f16* dst = out + (static_cast<int64_t>(s) * num_q_heads + h) * D;
   const int kvh = h / group, hg = h - kvh * group;
   const int NG = sh.num_groups;
+  // two rounds of loads: the sequence's context, group and own-part descriptor, then the
+  // group's arrays and prefix descriptor
   const int ctx = context_lens[s];
   const int gi = sh.seq_group[s];
+  const int sp = gi * n_units + kvh, so = (NG + s) * n_units + kvh;
+  const int2 dn0 = seg_desc[so];  // read whether or not there is an own part
   bool ok = ctx >= 0 && ctx <= max_context_len;
   int L = 0, f = 0;
+  int2 dp = make_int2(0, -1);
   if (gi >= 0) {
     ok = ok && gi < NG;
     if (ok) {  // the group arrays are read only at valid indexes (they may be empty)
       L = sh.group_prefix[gi];
       const int n = sh.group_size[gi];
       f = sh.group_first[gi];
+      dp = seg_desc[sp];
       ok = shared_group_ok(L, n, f, num_seqs, group, block_size, max_context_len) && s >= f && s < f + n &&
            L <= ctx;
     }
@@ -2579,9 +2595,7 @@ __global__ __launch_bounds__(kWave) void pa_shared_reduce_kernel(f16* __restrict
   // the two lists of pieces: the prefix segment (group gi, row (s - f) G + hg) and the own
   // segment (sequence s, row hg); a segment held whole by one wave has one piece, in the
   // record 2 waves + its segment index
-  const int sp = gi * n_units + kvh, so = (NG + s) * n_units + kvh;
-  const int2 dp = gi >= 0 ? seg_desc[sp] : make_int2(0, -1);
-  const int2 dn = ctx > L ? seg_desc[so] : make_int2(0, -1);
+  const int2 dn = ctx > L ? dn0 : make_int2(0, -1);
   const int np0 = dp.y - dp.x + 1, np1 = dn.y - dn.x + 1;
   const bool desc_ok = (gi < 0 || (dp.x >= 0 && dp.x <= dp.y && dp.y < waves)) &&
                        (ctx <= L || (dn.x >= 0 && dn.x <= dn.y && dn.y < waves));
