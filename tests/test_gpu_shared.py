@@ -125,6 +125,24 @@ def test_shared_short_prefixes_of_two_row_blocks(D, B):
     _fp16_bound(got, ref, case, label)
 
 
+@pytest.mark.parametrize("n_groups", [64, 70])
+def test_shared_many_groups(n_groups):
+    """Up to 64 groups, the kernels read every group's description in one round from the lanes;
+    past that, from memory after the sequence's group index: both against the oracle."""
+    layout = [("g", 16 * (1 + i % 3), [i % 5, (3 * i) % 7][: 1 + i % 2]) for i in range(n_groups)]
+    layout.insert(n_groups // 2, ("s", 37))
+    label = f"{n_groups} groups"
+    G.say(label)
+    case = W.shared_groups(layout, seed=16 + n_groups, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16)
+    assert len(case.meta["group_first"]) == n_groups
+    d = G.to_device(case)
+    got = _shared(case, d, _groups(case))
+    kc, vc = oracle_pools(case)
+    ref = oracle_decode(case, kc, vc)
+    G.assert_close(got, ref, np.float16, label)
+    _fp16_bound(got, ref, case, label)
+
+
 def test_shared_repeatable_bitwise():
     case = W.shared_groups(LAYOUTS[1], seed=7)
     d = G.to_device(case)
