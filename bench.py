@@ -4,9 +4,11 @@
 One step = the whole hot path over one batch: store every sequence's new token
 in its last block, then attend over the whole context.  For fp16 pools that is one
 pa_decode_append (the stream kernel, whose persistent waves each take an equal share of
-the batch's tiles and take the new tokens from their input rows, then the log-sum-exp
-reduce, which also stores the new tokens); for E4M3 and fp32 pools it is
-pa_cache_write(_fp8), then pa_decode(_fp8) (--step chooses).
+the batch's tiles, weighed for piece boundaries, and take the new tokens from their input
+rows, then the log-sum-exp reduce, which also stores the new tokens); for E4M3 and fp32
+pools it is pa_cache_write(_fp8), then pa_decode(_fp8) (--step chooses).  The shared-prefix
+batch steps with pa_cache_write + pa_decode_shared, which reads each group's prompt blocks
+once (--step fused: pa_decode_append, every sample reading the prompt).
 Default workload: a Llama-3-8B-shaped decode layer (64 sequences, 32 q / 8 kv
 heads, head_dim 128, block 16, context lengths uniform in [512, 4096], fp16,
 blocks scattered over a 1.2x pool).  Inputs are resident in HBM before timing.

@@ -109,9 +109,9 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * and 4.4).  A context of 0 gives a zero row.
  *
  * Work split: the batch is cut into tiles of consecutive tokens and persistent
- * waves each take an equal run of them, so a long context is split over several
- * waves; a second kernel merges the pieces of each context by log-sum-exp, in
- * token order.  partition_size == 0 uses as many waves as the GPU holds at once;
+ * waves each take a contiguous run of them (equal in tiles plus one tile's worth per
+ * context piece), so a long context is split over several waves; a second kernel
+ * merges the pieces of each context by log-sum-exp, in token order.  partition_size == 0 uses as many waves as the GPU holds at once;
  * partition_size > 0 (a multiple of block_size) adds waves until each takes about
  * that many tokens at most.  Results are bitwise identical under any relabelling of
  * physical blocks and any block size; where a context is split depends on the whole

@@ -3,7 +3,8 @@
 // Three kernels:
 //   pa_cache_write_kernel  -- scatter each new token's K/V row into its slot.
 //   pa_stream_kernel       -- attention over the paged K/V, the whole batch streamed
-//                             by persistent waves that each own an equal share of it.
+//                             by persistent waves that each own an equal share of it
+//                             (equal in tiles plus piece boundaries).
 //   pa_reduce_kernel       -- log-sum-exp merge of the pieces a context was split into.
 //
 // Sources (page title, section):
@@ -25,9 +26,10 @@
 //  * All G query heads that share a kv head are handled by one wave, so each K/V
 //    row is read from HBM once per group (GQA), not once per query head.
 //  * Work split ("stream-K"): the batch is flattened into tiles of consecutive tokens
-//    ordered by (sequence, kv head, position) and every persistent wave takes an
-//    equal, contiguous run of tiles.  A context split between waves leaves one
-//    partial result per piece; the reduce kernel merges the pieces by log-sum-exp.
+//    ordered by (sequence, kv head, position) and every persistent wave takes a
+//    contiguous run of them, the runs equal in tiles plus one tile's worth per segment
+//    they enter.  A context split between waves leaves one partial result per piece;
+//    the reduce kernel merges the pieces by log-sum-exp.
 //    Load balance is exact whatever the mix of context lengths.
 //  * Each wave keeps a two-stage ring in LDS filled by direct global->LDS loads, so
 //    two tiles are in flight during arithmetic without holding them in registers.
@@ -2234,8 +2236,8 @@ struct VWork {
 };
 
 // The shared-prefix stream kernel: the fp16 MFMA stream kernel (3-stage ring, persistent
-// waves, equal shares of the tile list) over the virtual sequences, with up to two 16-row
-// blocks of query rows per unit (NRB) and every piece written to a record.
+// waves, equal shares of the estimated cost, VWork) over the virtual sequences, with up to
+// two 16-row blocks of query rows per unit (NRB) and every piece written to a record.
 template <int D>
 __global__ __launch_bounds__(kWave) void pa_shared_mfma_kernel(const StreamArgs a, const SharedArgs sh) {
   using K = MCfg<D, false>;
