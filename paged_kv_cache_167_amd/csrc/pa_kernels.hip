@@ -2094,14 +2094,14 @@ struct VWork {
     A = 0;
     const int nch = (V + kWave - 1) / kWave;
     const bool cached = nch <= kChunks;
-    int k_ctx[kChunks], k_trow[kChunks], k_pos0[kChunks], k_s0[kChunks], k_rows[kChunks];
+    int k_ctx[kChunks] = {}, k_trow[kChunks] = {}, k_pos0[kChunks] = {}, k_s0[kChunks] = {}, k_rows[kChunks] = {};
     auto chunk = [&](int b, int& ctxv, int& trow, int& pos0, int& s0, int& rows) __attribute__((always_inline)) {
       int cv, gi, Lp, np, fp;
       geom_lanes1(b * kWave + lane, cv, gi, Lp, np, fp);
       geom_lanes2(b * kWave + lane, cv, gi, Lp, np, fp, ctxv, trow, pos0, s0, rows);
     };
     if (cached) {  // both rounds of loads of all chunks at once
-      int cv[kChunks], gi[kChunks], Lp[kChunks], np[kChunks], fp[kChunks];
+      int cv[kChunks] = {}, gi[kChunks] = {}, Lp[kChunks] = {}, np[kChunks] = {}, fp[kChunks] = {};
 #pragma unroll
       for (int b = 0; b < kChunks; ++b)
         if (b < nch) geom_lanes1(b * kWave + lane, cv[b], gi[b], Lp[b], np[b], fp[b]);
