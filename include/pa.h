@@ -86,10 +86,11 @@ int pa_cache_write(const void* k, const void* v, const int64_t* slot_mapping,
 /*
  * pa_decode_workspace_bytes -- workspace pa_decode needs for these sizes.
  *
- * The workspace holds, per (sequence, kv head, tile of query heads), which of the
- * decode's persistent waves hold pieces of that context, and per wave up to two
- * piece records (fp32 running max, exp-sum and normalised output of each query
- * head).  Its size depends only on the arguments below, never on the device.
+ * The workspace holds, per (sequence, kv head, tile of query heads), where that
+ * context's piece records are, and the records (fp32 running max, exp-sum and
+ * normalised output of each query head): up to two per persistent wave for
+ * partition_size == 0, one per partition of each context for partition_size > 0.
+ * Its size depends only on the arguments below, never on the device.
  * Returns 0 for num_seqs <= 0 or invalid sizes.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -108,14 +109,22 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * The result equals attention over contiguously stored K/V ([SOSP] sections 3.3
  * and 4.4).  A context of 0 gives a zero row.
  *
- * Work split: the batch is cut into tiles of consecutive tokens and persistent
- * waves each take a contiguous run of them (equal in tiles plus one tile's worth per
- * context piece), so a long context is split over several waves; a second kernel
- * merges the pieces of each context by log-sum-exp, in token order.  partition_size == 0 uses as many waves as the GPU holds at once;
- * partition_size > 0 (a multiple of block_size) adds waves until each takes about
- * that many tokens at most.  Results are bitwise identical under any relabelling of
- * physical blocks and any block size; where a context is split depends on the whole
- * batch, so the same sequence at another batch position may differ in rounding.
+ * Work split: the batch is cut into tiles of consecutive tokens and as many
+ * persistent waves as the GPU holds at once each take a contiguous run of them, so a
+ * long context is split over several waves; a second kernel merges the pieces of each
+ * context by log-sum-exp, in token order.
+ *   partition_size == 0: each wave's run is equal in tiles plus one tile's worth per
+ *     context piece, and a piece ends where a wave's run ends.  Where a context is
+ *     split then depends on the whole batch, so the same sequence at another batch
+ *     position may differ in rounding.
+ *   partition_size > 0 (a multiple of block_size and of 16): each context is cut into
+ *     fixed partitions of partition_size tokens (a split of this library's own; the
+ *     pages fix no split), a partition is never split between waves, and the runs are
+ *     balanced over tiles plus one tile's worth per partition.  A row's result then depends only on
+ *     its own query, context and partition_size: bitwise identical at any batch
+ *     position and in any batch.
+ * In both modes results are bitwise identical under any relabelling of physical blocks
+ * and any block size.
  * Arithmetic: fp32 scores, softmax and accumulation.  For PA_F16 the probabilities are
  * rounded to fp16 for the P.V product (on the matrix cores), which bounds the output's
  * deviation from exact attention by about 2^-11 * (|out| + max |v|).
@@ -507,7 +516,7 @@ const char* pa_last_error(void);
 
 /* ABI version of this header: (major << 16) | minor. */
 int pa_abi_version(void);
-#define PA_ABI_VERSION ((2 << 16) | 8)
+#define PA_ABI_VERSION ((2 << 16) | 9)
 
 #ifdef __cplusplus
 }

@@ -405,10 +405,12 @@ __global__ __launch_bounds__(256) void pa_cache_write_fp8_kernel(
 // it has ceil(ctx / TK) tiles.  Segments are ordered by sequence, then unit.
 struct StreamArgs {
   void* out;
-  int2* seg_desc;       // [S * n_units] {first wave, last wave} holding pieces of the segment
-  float* rec_m;         // [2 * W * rec_rows] per piece record: running max (log2 units) per row
-  float* rec_l;         // [2 * W * rec_rows] exp-sum per row
-  float* rec_o;         // [2 * W * rec_rows * D] normalised output per row
+  int2* seg_desc;       // [S * n_units] {first wave, last wave} holding pieces of the segment, or
+                        // with partitions {first partition record, partitions}
+  float* rec_m;         // [records * rec_rows] per piece record: running max (log2 units) per row
+  float* rec_l;         // [records * rec_rows] exp-sum per row
+  float* rec_o;         // [records * rec_rows * D] normalised output per row
+  int part_tiles;       // > 0: pieces are fixed partitions of this many tiles (one record each)
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -468,23 +470,31 @@ struct Cursor {
   int ctx;     // context length of the sequence
   int gstart;  // global index of the segment's first tile
   int seg;     // non-empty segments before this one
+  int p0;      // with partitions: the record of the segment's first partition
 };
 
 // The work split.  The batch is one list of tiles (TK consecutive tokens of one segment,
 // segments in order), and each wave takes an equal share of an estimated cost: a tile
-// costs one unit, and each non-empty segment one more (a piece boundary -- q rows, record,
-// cursor -- costs about as much as a tile on MI355X), so that a wave whose share crosses
-// more boundaries takes fewer tiles.  Tile x of a segment with j non-empty segments before
-// it sits at cost position x + j + 1; wave w takes the tiles at positions p with
-// floor(p Wp / total) = w, a contiguous range.  Wp = min(waves, total): every share is at
-// least one position wide, so no wave inside a segment's span is left without a tile of it
-// (the reduce takes one piece from each wave of a segment's {first, last} range).
+// costs one unit, and each piece boundary one more (a boundary -- q rows, record, cursor --
+// costs about as much as a tile on MI355X), so that a wave whose share crosses more
+// boundaries takes fewer tiles.
+//  * Default (part_tiles = 0): a boundary per non-empty segment.  Tile x of a segment with j
+//    non-empty segments before it sits at cost position x + j + 1; wave w takes the tiles at
+//    positions p with floor(p Wp / total) = w, a contiguous range.  Wp = min(waves, total):
+//    every share is at least one position wide, so every wave in a segment's {first, last}
+//    range holds a piece of it, as the reduce requires.
+//  * Partitions (part_tiles = PT > 0): each segment is cut into partitions of PT tiles (the
+//    last may be shorter), a boundary each, and whole partitions go to the waves: partition
+//    k, with first tile x and k partitions before it, sits at x + k + 1, and goes to wave
+//    floor(p Wp / total).  A partition is one piece with a record of its own, so a
+//    sequence's result does not depend on the rest of the batch or on the wave count.
 template <int TK>
 struct Work {
   const int32_t* ctxs;
   int S, max_ctx, n_units;
+  int PT;           // tiles per partition, 0: none
   int Wp;           // waves sharing the work
-  int total;        // tiles plus non-empty segments (the host bounds it below 2^31)
+  int total;        // tiles plus pieces (the host bounds it below 2^31)
   double inv_total;
   int A, n_my;      // this wave's share: tiles [A, A + n_my)
   int ctx0;         // this lane's context length among the first 64 sequences (0 past S): one
@@ -493,6 +503,13 @@ struct Work {
   __device__ int seg_tiles(int ctx) const {  // invalid or empty contexts contribute no tiles
     return (ctx > 0 && ctx <= max_ctx) ? (ctx + TK - 1) / TK : 0;
   }
+  __device__ int parts_of(int nt) const { return PT > 0 ? (nt + PT - 1) / PT : (nt > 0 ? 1 : 0); }
+  // pieces start and end at segment ends, and with partitions at partition ends
+  __device__ bool piece_starts(const Cursor& c) const { return c.t == 0 || (PT > 0 && c.t % PT == 0); }
+  __device__ bool piece_ends(const Cursor& c) const {
+    return c.t == c.nt - 1 || (PT > 0 && (c.t + 1) % PT == 0);
+  }
+  __device__ int part_record(const Cursor& c) const { return c.p0 + c.t / PT; }
 
   // floor(n / d) for 0 <= n < 2^53 and 0 < d < 2^31: a double estimate (off by at most one
   // for these sizes), corrected with exact integer products
@@ -509,17 +526,18 @@ struct Work {
     S = a.num_seqs;
     max_ctx = a.max_context_len;
     n_units = a.n_units;
+    PT = a.part_tiles;
     n_my = 0;
     A = 0;
     ctx0 = lane < S ? ctxs[lane] : 0;
-    int part = seg_tiles(ctx0), nseg = part > 0 ? 1 : 0;
+    int part = seg_tiles(ctx0), npc = parts_of(part);
     for (int b = kWave; b < S; b += kWave) {
       const int nt = (b + lane < S) ? seg_tiles(ctxs[b + lane]) : 0;
       part += nt;
-      nseg += nt > 0 ? 1 : 0;
+      npc += parts_of(nt);
     }
     const int T = wave_sum_int(part) * n_units;
-    total = T + wave_sum_int(nseg) * n_units;
+    total = T + wave_sum_int(npc) * n_units;
     Wp = min(a.num_waves, total);
     if (T == 0 || w >= Wp) return;
     inv_total = 1.0 / static_cast<double>(total);
@@ -527,37 +545,51 @@ struct Work {
     const int th0 = static_cast<int>(div_floor(static_cast<int64_t>(w) * total + Wp - 1, Wp, inv_wp));
     const int th1 =
         w + 1 == Wp ? total : static_cast<int>(div_floor(static_cast<int64_t>(w + 1) * total + Wp - 1, Wp, inv_wp));
-    // the first tiles at positions >= th0 and >= th1 (th1 = total: none, the end)
+    // the first tiles at positions >= th0 and >= th1 (th1 = total: none, the end); with
+    // partitions, the first tiles of the first partitions there
     int x0 = -1, x1 = T;
-    int base_t = 0, base_j = 0;  // tiles and non-empty segments before the chunk
+    int base_t = 0, base_j = 0;  // tiles and pieces (segments, or partitions) before the chunk
     for (int b = 0; b < S && x1 == T; b += kWave) {
       const int cl = b == 0 ? ctx0 : ((b + lane < S) ? ctxs[b + lane] : 0);
-      const int nt = seg_tiles(cl);
-      const int ts = nt * n_units, ss = nt > 0 ? n_units : 0;
+      const int nt = seg_tiles(cl), np = parts_of(nt);
+      const int ts = nt * n_units, ss = np * n_units;
       const int ti = wave_incl_scan_int(ts, lane), si = wave_incl_scan_int(ss, lane);
       const int Gs = base_t + ti - ts, Js = base_j + si - ss;
-      // the sequence's last tile sits at Gs + ts - 1 + Js + ss; the first sequence whose last
-      // tile reaches th holds the first tile at or past th
+      // the position of the sequence's last piece (the last tile of its last segment, or
+      // the first tile of its last partition); the first sequence whose last reaches th
+      // holds the first tile or partition at or past th
+      const int last = PT > 0 ? Gs + Js + (n_units - 1) * (nt + np) + (np - 1) * (PT + 1) + 1 : Gs + ts + Js + ss - 1;
       auto find = [&](int th, int& x, bool cursor) __attribute__((always_inline)) {
-        const uint64_t hit = __builtin_amdgcn_ballot_w64(nt > 0 && Gs + ts + Js + ss - 1 >= th);
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(nt > 0 && last >= th);
         if (hit == 0) return;
         const int l = __builtin_ctzll(hit);
-        const int ntl = __builtin_amdgcn_readlane(nt, l);
-        const int gj = __builtin_amdgcn_readlane(Gs, l) + __builtin_amdgcn_readlane(Js, l);
-        // unit u's last tile sits at gj + (u + 1)(nt + 1) - 1
-        const int ru = th - gj + 1;
-        const int u = ru > 0 ? max(0, (ru + ntl) / (ntl + 1) - 1) : 0;
-        const int rt = th - gj - u * (ntl + 1) - 1;  // tile t sits at gj + u (nt + 1) + t + 1
-        const int t = rt > 0 ? rt : 0;
-        x = __builtin_amdgcn_readlane(Gs, l) + u * ntl + t;
+        const int ntl = __builtin_amdgcn_readlane(nt, l), npl = __builtin_amdgcn_readlane(np, l);
+        const int Gl = __builtin_amdgcn_readlane(Gs, l), Jl = __builtin_amdgcn_readlane(Js, l);
+        const int gj = Gl + Jl;
+        int u, t;
+        if (PT > 0) {
+          // partition j of unit u sits at gj + u (nt + np) + j (PT + 1) + 1
+          const int ru = th - gj - (npl - 1) * (PT + 1) - 1;
+          u = ru > 0 ? (ru + ntl + npl - 1) / (ntl + npl) : 0;
+          const int rj = th - gj - u * (ntl + npl) - 1;
+          t = (rj > 0 ? (rj + PT) / (PT + 1) : 0) * PT;
+        } else {
+          // unit u's last tile sits at gj + (u + 1)(nt + 1) - 1, its tile t at gj + u (nt + 1) + t + 1
+          const int ru = th - gj + 1;
+          u = ru > 0 ? max(0, (ru + ntl) / (ntl + 1) - 1) : 0;
+          const int rt = th - gj - u * (ntl + 1) - 1;
+          t = rt > 0 ? rt : 0;
+        }
+        x = Gl + u * ntl + t;
         if (cursor) {
           c.s = b + l;
           c.ctx = __builtin_amdgcn_readlane(cl, l);
           c.nt = ntl;
           c.unit = u;
           c.t = t;
-          c.gstart = __builtin_amdgcn_readlane(Gs, l) + u * ntl;
-          c.seg = __builtin_amdgcn_readlane(Js, l) + u;
+          c.gstart = Gl + u * ntl;
+          c.seg = Jl + u;            // default split: non-empty segments before
+          c.p0 = Jl + u * npl;       // partitions: the segment's first partition
         }
       };
       if (x0 < 0) find(th0, x0, true);
@@ -569,7 +601,7 @@ struct Work {
     n_my = x0 < 0 ? 0 : x1 - x0;
   }
 
-  // the wave holding the last tile of c's segment
+  // the wave holding the last tile of c's segment (default split)
   __device__ int wave_of_last(const Cursor& c) const {
     const int p = c.gstart + c.nt - 1 + c.seg + 1;
     return static_cast<int>(div_floor(static_cast<int64_t>(p) * Wp, total, inv_total));
@@ -578,6 +610,7 @@ struct Work {
   __device__ void advance(Cursor& c) const {
     if (++c.t < c.nt) return;
     c.gstart += c.nt;
+    c.p0 += parts_of(c.nt);
     c.t = 0;
     ++c.seg;
     if (++c.unit < n_units) return;
@@ -707,6 +740,7 @@ template <typename T, int D, int GT>
 __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   using K = Cfg<T, D, GT>;
   constexpr int RK = K::kRK, NL = K::kNL, DL = K::kDL, C = K::kC, E = K::kE, TK = K::kTK;
+  static_assert(16 % TK == 0, "partitions are whole multiples of 16 tokens: whole tiles");
   constexpr int GR = K::kGroups;
   __shared__ __align__(16) u32x4 s_stage0[8][kWave];
   __shared__ __align__(16) u32x4 s_stage1[8][kWave];
@@ -811,7 +845,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     }
     piece_bad = false;
     if (cc.t == 0 && lane == 0)  // this wave starts the segment: record who holds its pieces
-      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of_last(cc));
+      a.seg_desc[cc.s * a.n_units + cc.unit] =
+          a.part_tiles > 0 ? make_int2(cc.p0, wk.parts_of(cc.nt)) : make_int2(w, wk.wave_of_last(cc));
     // Wait for the q rows here, once per piece.  Left to the compiler, the wait lands at
     // the first use of q on every tile (it cannot tell whether this branch ran) and would
     // drain the K/V loads in flight each time.
@@ -925,11 +960,13 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     }
     // lanes 0..C-1 now hold the piece's state for their chunks of the row
     if (grp != 0) return;
-    const bool whole = cc.gstart >= A && cc.gstart + cc.nt <= A_end;
+    // with partitions, a record per partition; rows only for a context of one partition
+    const bool part = a.part_tiles > 0;
+    const bool whole = part ? wk.parts_of(cc.nt) == 1 : cc.gstart >= A && cc.gstart + cc.nt <= A_end;
     const bool head = cc.gstart < A;  // the segment began in an earlier wave
     const float qnan = __builtin_nanf("");
     const int64_t row0 = static_cast<int64_t>(cc.s) * a.num_q_heads + h0;
-    const int rec = w * 2 + (head ? 0 : 1);
+    const int rec = part ? wk.part_record(cc) : w * 2 + (head ? 0 : 1);
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
       if (g >= ng) break;
@@ -957,10 +994,10 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
   };
 
   auto process = [&](int i, const u32x4 (&kb)[RK][NL], u32x4 (&vb)[RK][NL], bool stage_bad) {
-    if (i == 0 || cc.t == 0) piece_start();
+    if (i == 0 || wk.piece_starts(cc)) piece_start();
     piece_bad |= stage_bad;
     consume(min(TK, cc.ctx - cc.t * TK), kb, vb);
-    if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
+    if (i == n_my - 1 || wk.piece_ends(cc)) piece_end();
     advance(cc);
   };
 
@@ -1653,23 +1690,28 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   int h0 = 0, ng = 0;
   bool piece_bad = false;
 
-  // Start a piece at the current tile, whose stage stc holds the piece's q rows.
-  auto piece_start = [&](auto stc) __attribute__((always_inline)) {
+  // Start a piece at the current tile.  qread: the tile starts the wave's share or its
+  // segment, and its stage stc holds the segment's q rows (a later partition of the same
+  // segment keeps them).
+  auto piece_start = [&](auto stc, bool qread) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
-    const int kvh = cc.unit / a.n_gtiles;
-    const int gtile = cc.unit - kvh * a.n_gtiles;
-    h0 = kvh * a.group + gtile * kMfRows;
-    ng = min(kMfRows, a.group - gtile * kMfRows);
-    read_q_mf<KB, st * STAGE + QOFF>(qa, qop);
+    if (qread) {
+      const int kvh = cc.unit / a.n_gtiles;
+      const int gtile = cc.unit - kvh * a.n_gtiles;
+      h0 = kvh * a.group + gtile * kMfRows;
+      ng = min(kMfRows, a.group - gtile * kMfRows);
+      read_q_mf<KB, st * STAGE + QOFF>(qa, qop);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qop[kb] = g < ng ? qop[kb] : f16x8{};
+      for (int kb = 0; kb < KB; ++kb) qop[kb] = g < ng ? qop[kb] : f16x8{};
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     m = -INFINITY;
     l = 0.0f;
     piece_bad = false;
-    if (cc.t == 0 && lane == 0)
-      a.seg_desc[cc.s * a.n_units + cc.unit] = make_int2(w, wk.wave_of_last(cc));
+    if (cc.t == 0 && lane == 0)  // who holds the segment's pieces
+      a.seg_desc[cc.s * a.n_units + cc.unit] =
+          a.part_tiles > 0 ? make_int2(cc.p0, wk.parts_of(cc.nt)) : make_int2(w, wk.wave_of_last(cc));
   };
 
   auto consume = [&](int cn, const f16x8 (&kop)[KB], f16x4 (&vop)[NB]) __attribute__((always_inline)) {
@@ -1738,12 +1780,14 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
       lt = as_f(x16[0]) + as_f(x16[1]);
     }
     if (g >= ng) return;
-    const bool whole = cc.gstart >= A && cc.gstart + cc.nt <= A_end;
+    // with partitions, a record per partition; rows only for a context of one partition
+    const bool part = a.part_tiles > 0;
+    const bool whole = part ? wk.parts_of(cc.nt) == 1 : cc.gstart >= A && cc.gstart + cc.nt <= A_end;
     const bool head = cc.gstart < A;
     const float qnan = __builtin_nanf("");
     const float inv = piece_bad ? qnan : (F8 ? a.out_scale / lt : 1.0f / lt);
     const int64_t row = static_cast<int64_t>(cc.s) * a.num_q_heads + h0 + g;
-    const int rec = w * 2 + (head ? 0 : 1);
+    const int rec = part ? wk.part_record(cc) : w * 2 + (head ? 0 : 1);
     if constexpr (F8) {
       // o[nb][r] is dim NB (4 jq + r) + nb: the lane holds dims 4 NB jq .. 4 NB jq + 4 NB - 1
 #pragma unroll
@@ -1793,7 +1837,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   const uint32_t nv_addr = ring + static_cast<uint32_t>(2 * NB * g);
   auto process = [&](int i, auto stc) __attribute__((always_inline)) {
     constexpr int st = decltype(stc)::value;
-    if (i == 0 || cc.t == 0) piece_start(stc);
+    if (i == 0 || wk.piece_starts(cc)) piece_start(stc, i == 0 || cc.t == 0);
     piece_bad |= fbad[st];
     if constexpr (F8NEW) {
       if (cc.t == cc.nt - 1) {  // the segment's last tile holds the new token, row rn
@@ -1825,7 +1869,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
       }
     }
     consume(min(TK, cc.ctx - cc.t * TK), kop, vop);
-    if (i == n_my - 1 || cc.t == cc.nt - 1) piece_end();
+    if (i == n_my - 1 || wk.piece_ends(cc)) piece_end();
     wk.advance(cc);
   };
 
@@ -3086,7 +3130,7 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
     T* __restrict__ out, const int2* __restrict__ seg_desc, const float* __restrict__ rec_m,
     const float* __restrict__ rec_l, const float* __restrict__ rec_o,
     const int32_t* __restrict__ context_lens, int num_q_heads, int group, int n_gtiles,
-    int max_context_len, int w_cap, int rec_rows, const AppendArgs ap) {
+    int max_context_len, int w_cap, int rec_rows, int parts, int64_t rec_cap, const AppendArgs ap) {
   constexpr int kDPL = D / kWave;  // dims per lane
   const int h = blockIdx.x;
   const int s = blockIdx.y;
@@ -3133,6 +3177,16 @@ __global__ __launch_bounds__(kWave) void pa_reduce_kernel(
     const T fill = static_cast<T>(ctx == 0 ? 0.0f : __builtin_nanf(""));
 #pragma unroll
     for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = fill;
+    return;
+  }
+  if (parts) {  // fixed partitions: d = {first partition's record, partitions}
+    if (d.y == 1) return;  // one partition: the stream kernel wrote the row
+    if (d.x < 0 || d.y < 1 || static_cast<int64_t>(d.x) + d.y > rec_cap) {  // not written by the stream kernel
+#pragma unroll
+      for (int k = 0; k < kDPL; ++k) dst[k * kWave + lane] = static_cast<T>(__builtin_nanf(""));
+      return;
+    }
+    merge_indexed<T, D>(dst, rec_m, rec_l, rec_o, d.y, [&](int p) { return (d.x + p) * rec_rows + g; }, lane);
     return;
   }
   if (d.x == d.y) return;  // one wave held the whole segment and wrote the row
@@ -3186,23 +3240,22 @@ int group_tile(int group, int dtype) {
   return group >= 5 ? 8 : group >= 3 ? 4 : group;
 }
 
-constexpr int64_t kWaveCap = static_cast<int64_t>(1) << 25;  // waves of one stream launch
-
 // Geometry shared by the size query, the stream launch and the reduce launch.
 struct Geom {
   int gt = 1;        // query heads per unit
   int n_gtiles = 1;  // units per kv head
   int n_units = 1;   // segments per sequence
   int rec_rows = 1;  // query rows per piece record
-  int w_cap = 1;     // waves the workspace has records for
+  int w_cap = 1;     // waves a launch may use (the default split's records are per wave)
+  int part = 0;      // fixed partitions: one record per partition
+  int64_t rec_cap = 0;  // piece records in the workspace
   size_t desc_bytes = 0, rec_ml_bytes = 0, rec_o_bytes = 0, ws_bytes = 0;
 };
 
-// Waves asked for by partition_size > 0: enough that no wave takes much more than
-// partition_size tokens of one unit (the batch holds at most S * units * max_ctx).
-int64_t waves_for_partition(int64_t num_seqs, int n_units, int max_context_len, int partition_size) {
-  if (partition_size <= 0) return 0;
-  return (num_seqs * n_units * static_cast<int64_t>(max_context_len) + partition_size - 1) / partition_size;
+void size_records(Geom& g, int head_dim) {
+  g.rec_ml_bytes = align256(static_cast<size_t>(g.rec_cap) * g.rec_rows * sizeof(float));
+  g.rec_o_bytes = align256(static_cast<size_t>(g.rec_cap) * g.rec_rows * head_dim * sizeof(float));
+  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
 }
 
 Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -3212,25 +3265,26 @@ Geom geometry(int64_t num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
   g.gt = group_tile(group, dtype);
   g.n_gtiles = (group + g.gt - 1) / g.gt;
   g.n_units = num_kv_heads * g.n_gtiles;
-  int64_t w = kMaxWaves;
-  const int64_t want = waves_for_partition(num_seqs, g.n_units, max_context_len, partition_size);
-  if (want > w) w = want;
-  g.w_cap = static_cast<int>(w > kWaveCap ? kWaveCap : w);  // one-wave groups: 2^31 work-items at most
+  g.w_cap = kMaxWaves;
   g.rec_rows = g.gt < group ? g.gt : group;
   g.desc_bytes = align256(static_cast<size_t>(num_seqs) * g.n_units * 2 * sizeof(int));
-  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * sizeof(float));
-  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * head_dim * sizeof(float));
-  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
+  // default split: a head and a tail record per wave; partitions: one per partition, at most
+  // ceil(max_ctx / partition_size) per segment
+  g.part = partition_size > 0 ? 1 : 0;
+  g.rec_cap = g.part ? std::max<int64_t>(1, num_seqs * g.n_units *
+                                                ((static_cast<int64_t>(max_context_len) + partition_size - 1) /
+                                                 partition_size))
+                     : static_cast<int64_t>(2) * g.w_cap;
+  size_records(g, head_dim);
   return g;
 }
 
-// The same layout with records for exactly `waves` waves (at most g.w_cap): the smallest
-// scratch one launch of that many waves needs.
+// The same layout for exactly `waves` waves (at most g.w_cap): the smallest scratch one
+// launch of that many waves needs (the per-partition records do not depend on the waves).
 Geom with_waves(Geom g, int waves, int head_dim) {
   g.w_cap = waves;
-  g.rec_ml_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * sizeof(float));
-  g.rec_o_bytes = align256(static_cast<size_t>(2) * g.w_cap * g.rec_rows * head_dim * sizeof(float));
-  g.ws_bytes = g.desc_bytes + 2 * g.rec_ml_bytes + g.rec_o_bytes;
+  if (!g.part) g.rec_cap = static_cast<int64_t>(2) * waves;
+  size_records(g, head_dim);
   return g;
 }
 
@@ -3273,8 +3327,9 @@ int check_decode(const DecodeCall& c, Geom* g, bool need_ws = true) {
   if (static_cast<int64_t>(c.max_context_len) > static_cast<int64_t>(c.max_blocks_per_seq) * c.block_size)
     return fail(PA_ERR_INVALID_ARG, "max_context_len %d exceeds max_blocks_per_seq * block_size = %lld",
                 c.max_context_len, (long long)c.max_blocks_per_seq * c.block_size);
-  if (c.partition_size < 0 || c.partition_size % c.block_size != 0)
-    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of block_size %d",
+  if (c.partition_size < 0 || c.partition_size % c.block_size != 0 || c.partition_size % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG,
+                "partition_size %d must be 0 or a positive multiple of 16 and of block_size %d",
                 c.partition_size, c.block_size);
   if (c.num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", c.num_seqs);
   if (c.num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", c.num_q_heads);
@@ -3286,6 +3341,9 @@ int check_decode(const DecodeCall& c, Geom* g, bool need_ws = true) {
   if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8 + 1) >
       (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
+  if (g->rec_cap * g->rec_rows > (static_cast<int64_t>(1) << 31) - 1)  // record rows are 32-bit indexes
+    return fail(PA_ERR_INVALID_ARG, "too many partitions: %lld records of %d rows", (long long)g->rec_cap,
+                g->rec_rows);
   if (c.num_blocks > (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "num_blocks above 2^31 - 1");
   if (static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim * (c.kv_fp8 ? 1 : c.dtype == PA_F16 ? 2 : 4) >
@@ -3376,12 +3434,9 @@ Residency residency(const void* kernel) {
   return r;
 }
 
-// Waves of one launch: `base` (the default split), raised with partition_size > 0;
-// never more than the workspace has records for.
-int waves_for(const DecodeCall& c, const Geom& g, int64_t base) {
+// Waves of one launch: `base`, never more than the workspace allows.
+int waves_for(const DecodeCall&, const Geom& g, int64_t base) {
   int64_t w = base > 0 ? base : kMaxWaves;
-  const int64_t want = waves_for_partition(c.num_seqs, g.n_units, c.max_context_len, c.partition_size);
-  if (want > w) w = want;
   if (w > g.w_cap) w = g.w_cap;
   return static_cast<int>(w < 1 ? 1 : w);
 }
@@ -3437,6 +3492,7 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   a.num_blocks = c.num_blocks;
   a.num_waves = 1;
   a.rec_rows = g.rec_rows;
+  a.part_tiles = 0;  // set by the launch, from its kernel's tile
   a.dense_k = a.dense_v = a.guard_k = a.guard_v = nullptr;
   a.seq_bytes = a.token_bytes = 0;
   if (c.dense) {
@@ -3457,6 +3513,7 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
 template <typename T, int D, int GT>
 int launch_stream(const DecodeCall& c, const Geom& g) {
   StreamArgs a = stream_args(c, g);
+  a.part_tiles = c.partition_size / Cfg<T, D, GT>::kTK;  // a multiple of 16 tokens: whole tiles
   a.num_waves = waves_valu<T, D, GT>(c, g);
   if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_kernel failed");
   hipLaunchKernelGGL((pa_stream_kernel<T, D, GT>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
@@ -3467,6 +3524,7 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
 template <int D, int NST, bool F8, bool DENSE = false, bool APPEND = false>
 int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
+  a.part_tiles = c.partition_size / MCfg<D, F8>::kTK;  // a multiple of 16 tokens: whole tiles
   a.num_waves = waves_mfma<D, NST, F8, DENSE, APPEND>(c, g, waves_per_cu);
   if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_mfma_kernel failed");
   hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>), dim3(a.num_waves), dim3(kWave), 0, c.stream,
@@ -3495,7 +3553,7 @@ int launch_reduce(const DecodeCall& c, const Geom& g) {
   hipLaunchKernelGGL((pa_reduce_kernel<T, D, GT>), dim3(c.num_q_heads, c.num_seqs), dim3(kWave), 0,
                      c.stream, static_cast<T*>(c.out), ws.desc, ws.rec_m, ws.rec_l, ws.rec_o,
                      c.context_lens, c.num_q_heads, c.num_q_heads / c.num_kv_heads, g.n_gtiles,
-                     c.max_context_len, g.w_cap, g.rec_rows, ap);
+                     c.max_context_len, g.w_cap, g.rec_rows, g.part, g.rec_cap, ap);
   return check_hip("pa_reduce_kernel launch");
 }
 
@@ -3833,10 +3891,15 @@ int pa_decode_reduce(void* out, const int32_t* context_lens, int32_t num_seqs,
     return fail(PA_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", num_q_heads, num_kv_heads);
   if (num_seqs > 65535) return fail(PA_ERR_INVALID_ARG, "num_seqs %d > 65535", num_seqs);
   if (num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", num_q_heads);
+  if (partition_size % 16 != 0)
+    return fail(PA_ERR_INVALID_ARG, "partition_size %d must be 0 or a positive multiple of 16", partition_size);
   if (num_seqs == 0) return PA_OK;
   const Geom g = geometry(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size, dtype);
   if (static_cast<int64_t>(num_seqs) * g.n_units > (static_cast<int64_t>(1) << 31) - 1)
     return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 segments");
+  if (g.rec_cap * g.rec_rows > (static_cast<int64_t>(1) << 31) - 1)  // record rows are 32-bit indexes
+    return fail(PA_ERR_INVALID_ARG, "too many partitions: %lld records of %d rows", (long long)g.rec_cap,
+                g.rec_rows);
   if (!out || !context_lens) return fail(PA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned(out, 16) || !aligned(context_lens, 4)) return fail(PA_ERR_INVALID_ARG, "misaligned pointer");
   if (!workspace) return fail(PA_ERR_WORKSPACE, "workspace is NULL, %zu bytes needed", g.ws_bytes);

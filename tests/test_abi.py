@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert P.lib().pa_abi_version() == (2 << 16) | 8
+    assert P.lib().pa_abi_version() == (2 << 16) | 9
 
 
 def test_workspace_size_query():
@@ -58,10 +58,10 @@ def test_workspace_size_query():
     assert P.pa_decode_workspace_bytes(S, hq, hkv, d, 4096, 0) == layout(S, hkv, waves, 4, d)
     # 56 query / 8 kv heads: groups of 7, one unit per kv head
     assert P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 0) == layout(8, 8, waves, 7, d)
-    # a partition size asks for more waves once the batch exceeds 4096 of them
+    # fixed partitions: one record per partition, ceil(max_ctx / partition_size) per segment
     big = P.pa_decode_workspace_bytes(8, 56, 8, d, 131072, 512)
-    waves_p = (8 * 8 * 131072 + 511) // 512
-    assert big == layout(8, 8, waves_p, 7, d)
+    recs = 8 * 8 * ((131072 + 511) // 512)
+    assert big == al(8 * 8 * 8) + 2 * al(recs * 7 * 4) + al(recs * 7 * d * 4)
     # 64 query heads per kv head: four units of 16 rows (fp16) or eight of 8 (fp32)
     wide = P.pa_decode_workspace_bytes(2, 64, 1, d, 1024, 0)
     assert wide == max(layout(2, 4, waves, 16, d), layout(2, 8, waves, 8, d))
@@ -90,6 +90,7 @@ def _decode(**over):
     (dict(hkv=0), _lib.PA_ERR_INVALID_ARG),
     (dict(S=-1), _lib.PA_ERR_INVALID_ARG),
     (dict(P=24), _lib.PA_ERR_INVALID_ARG),           # not a multiple of the block size
+    (dict(B=8, P=8), _lib.PA_ERR_INVALID_ARG),       # a multiple of the block size, not of 16
     (dict(mcl=257), _lib.PA_ERR_INVALID_ARG),        # beyond max_blocks * block_size
     (dict(N=0), _lib.PA_ERR_INVALID_ARG),
     (dict(q=FAKE + 8), _lib.PA_ERR_INVALID_ARG),     # misaligned
@@ -245,6 +246,12 @@ def test_reduce_rejects_bad_arguments():
     # more than 2^31 - 1 segments (sequence x kv head), whatever the workspace
     assert lib.pa_decode_reduce(FAKE, FAKE, 65535, 40000, 40000, 64, 0, 0, 1, FAKE, 1 << 50, None) == \
         _lib.PA_ERR_INVALID_ARG
+    # partition size not a multiple of 16; partitions whose record rows overflow 32 bits
+    assert lib.pa_decode_reduce(FAKE, FAKE, 4, 32, 8, 128, 4096, 24, 1, FAKE, 1 << 30, None) == \
+        _lib.PA_ERR_INVALID_ARG
+    assert lib.pa_decode_reduce(FAKE, FAKE, 64, 32, 8, 128, 1 << 30, 16, 1, FAKE, 1 << 62, None) == \
+        _lib.PA_ERR_INVALID_ARG
+    assert "too many partitions" in P.last_error()
     assert lib.pa_decode_reduce(FAKE, FAKE, 0, 32, 8, 128, 4096, 0, 1, None, 0, None) == _lib.PA_OK
 
 

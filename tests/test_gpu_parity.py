@@ -4,9 +4,9 @@ Writes must match byte for byte; attention must be within |d| <= 2e-3 + 1e-2|ref
 and the normalised error bound, and fp16 results also within the bound that the fp16
 rounding of probabilities and outputs implies.  Exact invariants (physical relabelling,
 context 1, padding poison, block size, split launches, repeat runs) are checked bitwise
-on the GPU.  Where a context is cut between waves depends on the whole batch, so the same
-sequence at another batch position (duplicated rows, a changed neighbour) is checked to
-within that rounding bound.
+on the GPU.  With the default split, where a context is cut between waves depends on the
+whole batch, so the same sequence at another batch position (duplicated rows, a changed
+neighbour) is checked to within that rounding bound; with fixed partitions it is bitwise.
 """
 import functools
 
@@ -223,6 +223,33 @@ def test_duplicated_rows_within_rounding():
     _within_rounding(got[1], full[0], case.dtype, "seq 0", vm)
 
 
+@pytest.mark.parametrize("dtype,partition", [(np.float16, 512), (np.float16, 64),
+                                             (np.float32, 512), (np.float16, 16)])
+def test_fixed_partitions_are_independent_of_the_batch(dtype, partition):
+    """With partition_size > 0 a context is cut at fixed multiples of the partition size
+    and each partition is one piece: a row does not depend on its batch position or on the
+    rest of the batch, so duplicated, reordered and lone sequences agree bitwise."""
+    torch = _torch()
+    case = _mid_case(dtype=dtype)
+    d = G.to_device(case)
+    full = G.decode(case, d, partition_size=partition)
+
+    def sub(rows):
+        idx = torch.tensor(rows, device="cuda")
+        return G.decode(case, d, partition_size=partition, q=d.q[idx].contiguous(),
+                        tables=d.tables[idx].contiguous(), ctx=d.ctx[idx].contiguous())
+
+    got = sub([5, 0, 5, 3, 5, 4])
+    for j, s in enumerate([5, 0, 5, 3, 5, 4]):
+        assert got[j].tobytes() == full[s].tobytes(), f"P{partition}: batch row {j} (seq {s})"
+    for s in (5, 4, 0):
+        assert sub([s])[0].tobytes() == full[s].tobytes(), f"P{partition}: seq {s} alone"
+    rev = sub(list(range(case.num_seqs))[::-1])
+    assert rev[::-1].tobytes() == full.tobytes(), f"P{partition}: reversed batch"
+    kc, vc = oracle_pools(case)
+    G.assert_close(full, oracle_decode(case, kc, vc), dtype, f"P{partition}")
+
+
 def test_shared_prompt_blocks_agree_for_identical_queries():
     torch = _torch()
     case = _config("shared_prefix", "plain")
@@ -366,9 +393,9 @@ def test_one_context_split_over_every_wave():
     _fp16_bound(got, ref, case, "200K context")
 
 
-def test_more_waves_than_the_gpu_holds():
-    """A 32-token partition asks for about 4500 waves, several per resident slot: results
-    agree with the oracle and, within rounding, with the default split."""
+def test_many_small_partitions():
+    """32-token partitions cut the 3001-token context into 94 pieces, merged by the second
+    launch: results agree with the oracle and, within rounding, with the default split."""
     case = _mid_case()
     d = G.to_device(case)
     got = G.decode(case, d, partition_size=32)
