@@ -98,32 +98,64 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ int wave_sum_int(int x) {
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return __builtin_amdgcn_readfirstlane(x);
+// Wave-wide scans and reductions in registers: DPP row operations within each row of 16
+// lanes, then across rows (row broadcasts for the scan, the permlane swaps, which pair lanes
+// i, i ^ 32 and i, i ^ 16, for reductions).  Shuffles would take an LDS round trip per step.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_or_zero(int x) {  // lanes with no source, or outside ROWS: 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u(unsigned x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ int wave_incl_scan_int(int x, int lane) {
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+// op over all 64 lanes, result in every lane; op on the 32-bit patterns (as unsigned)
+template <typename F>
+__device__ __forceinline__ unsigned wave_all(unsigned x, F op) {
+  x = op(x, dpp_u<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_u<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_u<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_u<0x140>(x));  // row_mirror: the row's result in all its lanes
+  const auto a = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  x = op(a[0], a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op(b[0], b[1]);
+}
+
+__device__ __forceinline__ int wave_sum_int(int x) {
+  const unsigned r = wave_all(static_cast<unsigned>(x), [](unsigned u, unsigned v) { return u + v; });
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(r));
+}
+
+// inclusive prefix sum over the lanes
+__device__ __forceinline__ int wave_incl_scan_int(int x) {
+  x += dpp_or_zero<0x111, 0xF>(x);  // row_shr:1
+  x += dpp_or_zero<0x112, 0xF>(x);  // row_shr:2
+  x += dpp_or_zero<0x114, 0xF>(x);  // row_shr:4
+  x += dpp_or_zero<0x118, 0xF>(x);  // row_shr:8: the scan within each row
+  x += dpp_or_zero<0x142, 0xA>(x);  // row_bcast:15: rows 1 and 3 add the row before
+  x += dpp_or_zero<0x143, 0xC>(x);  // row_bcast:31: rows 2 and 3 add rows 0-1
   return x;
 }
 
 __device__ __forceinline__ int wave_min_int(int x) {
-  for (int o = kWave / 2; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return __builtin_amdgcn_readfirstlane(x);
+  const unsigned r = wave_all(static_cast<unsigned>(x), [](unsigned u, unsigned v) {
+    return static_cast<unsigned>(min(static_cast<int>(u), static_cast<int>(v)));
+  });
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(r));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
-  for (int o = kWave / 2; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  return __builtin_bit_cast(float, wave_all(__builtin_bit_cast(unsigned, x), [](unsigned u, unsigned v) {
+    return __builtin_bit_cast(unsigned, fmaxf(__builtin_bit_cast(float, u), __builtin_bit_cast(float, v)));
+  }));
 }
 
 __device__ __forceinline__ float wave_sum(float x) {
-  for (int o = kWave / 2; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  return __builtin_bit_cast(float, wave_all(__builtin_bit_cast(unsigned, x), [](unsigned u, unsigned v) {
+    return __builtin_bit_cast(unsigned, __builtin_bit_cast(float, u) + __builtin_bit_cast(float, v));
+  }));
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {
@@ -553,7 +585,7 @@ struct Work {
       const int cl = b == 0 ? ctx0 : ((b + lane < S) ? ctxs[b + lane] : 0);
       const int nt = seg_tiles(cl), np = parts_of(nt);
       const int ts = nt * n_units, ss = np * n_units;
-      const int ti = wave_incl_scan_int(ts, lane), si = wave_incl_scan_int(ss, lane);
+      const int ti = wave_incl_scan_int(ts), si = wave_incl_scan_int(ss);
       const int Gs = base_t + ti - ts, Js = base_j + si - ss;
       // the position of the sequence's last piece (the last tile of its last segment, or
       // the first tile of its last partition); the first sequence whose last reaches th
@@ -2197,7 +2229,7 @@ struct VWork {
       }
       const int nt = tiles(ctxv), wt = tile_cost(rows);
       const int tl = nt * n_units, cost = nt > 0 ? n_units * (kShSegCost + nt * wt) : 0;
-      const int ti = wave_incl_scan_int(tl, lane), ci = wave_incl_scan_int(cost, lane);
+      const int ti = wave_incl_scan_int(tl), ci = wave_incl_scan_int(cost);
       const int Gv = base_t + ti - tl, Cv = base_c + ci - cost;
       // v's last tile sits at Cv + cost - wt; the first v whose last tile reaches th holds it
       auto find = [&](int th, int& x, bool cursor) __attribute__((always_inline)) {

@@ -261,6 +261,11 @@ def test_shared_prompt_blocks_agree_for_identical_queries():
     got = G.decode(case, d, q=q.contiguous(), tables=d.tables[:8].contiguous(), ctx=ctx)
     for s in range(1, 8):
         _within_rounding(got[s], got[0], case.dtype, f"sample {s}", _vmax(case))
+    # with fixed partitions the samples are bitwise equal
+    got = G.decode(case, d, q=q.contiguous(), tables=d.tables[:8].contiguous(), ctx=ctx,
+                   partition_size=512)
+    for s in range(1, 8):
+        assert got[s].tobytes() == got[0].tobytes(), f"sample {s}, partition 512"
 
 
 def test_padding_poison_has_no_effect():
