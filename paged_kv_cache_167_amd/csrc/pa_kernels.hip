@@ -71,6 +71,11 @@ constexpr int kMfWavesPerCU = 4;  // persistent fp16 waves per compute unit in t
 constexpr int kMfStages = 3;      // LDS ring depth of the fp16 kernel
 constexpr int kF8WavesPerCU = 8;  // E4M3 pools: tiles carry half the bytes, so more waves
 constexpr int kF8Stages = 2;      // with a shallower ring keep more loads in flight per CU
+// One-wave work-groups go to the eight dies in turn, so wave w runs on die w mod 8.  The
+// odd-numbered dies of MI355X stream K/V 4-8 % slower than the even ones (measured per die on
+// several boards), so the stream kernels give an odd-numbered wave a share of this weight
+// (of 64) against an even one's.
+constexpr int kOddDieWeight = 60;
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -506,20 +511,23 @@ struct Cursor {
 };
 
 // The work split.  The batch is one list of tiles (TK consecutive tokens of one segment,
-// segments in order), and each wave takes an equal share of an estimated cost: a tile
-// costs one unit, and each piece boundary one more (a boundary -- q rows, record, cursor --
-// costs about as much as a tile on MI355X), so that a wave whose share crosses more
-// boundaries takes fewer tiles.
+// segments in order), and each wave takes a share of an estimated cost: a tile costs one
+// unit, and each piece boundary one more (a boundary -- q rows, record, cursor -- costs
+// about as much as a tile on MI355X), so that a wave whose share crosses more boundaries
+// takes fewer tiles.  The shares are weighted by die: wave w takes the positions
+// [th(w), th(w + 1)), th(v) = ceil(cum_weight(v) total / Om), an odd-numbered wave weighing
+// kOddDieWeight / 64 of an even one (equal weights for batches under two positions a wave).
 //  * Default (part_tiles = 0): a boundary per non-empty segment.  Tile x of a segment with j
-//    non-empty segments before it sits at cost position x + j + 1; wave w takes the tiles at
-//    positions p with floor(p Wp / total) = w, a contiguous range.  Wp = min(waves, total):
-//    every share is at least one position wide, so every wave in a segment's {first, last}
-//    range holds a piece of it, as the reduce requires.
+//    non-empty segments before it sits at cost position x + j + 1, and a share is a
+//    contiguous range of tiles.  Wp = min(waves, total): every share is at least one
+//    position wide, so every wave in a segment's {first, last} range holds a piece of it, as
+//    the reduce requires.
 //  * Partitions (part_tiles = PT > 0): each segment is cut into partitions of PT tiles (the
 //    last may be shorter), a boundary each, and whole partitions go to the waves: partition
-//    k, with first tile x and k partitions before it, sits at x + k + 1, and goes to wave
-//    floor(p Wp / total).  A partition is one piece with a record of its own, so a
-//    sequence's result does not depend on the rest of the batch or on the wave count.
+//    k, with first tile x and k partitions before it, sits at x + k + 1, and goes to the
+//    wave whose share holds that position.  A partition is one piece with a record of its
+//    own, so a sequence's result does not depend on the rest of the batch or on the wave
+//    count.
 template <int TK>
 struct Work {
   const int32_t* ctxs;
@@ -528,6 +536,9 @@ struct Work {
   int Wp;           // waves sharing the work
   int total;        // tiles plus pieces (the host bounds it below 2^31)
   double inv_total;
+  int wo;           // share weight (of 64) of an odd-numbered wave
+  int64_t Om;       // total weight of the Wp waves
+  double inv_om;
   int A, n_my;      // this wave's share: tiles [A, A + n_my)
   int ctx0;         // this lane's context length among the first 64 sequences (0 past S): one
                     // load serves the totals and the scan
@@ -542,6 +553,10 @@ struct Work {
     return c.t == c.nt - 1 || (PT > 0 && (c.t + 1) % PT == 0);
   }
   __device__ int part_record(const Cursor& c) const { return c.p0 + c.t / PT; }
+  // summed share weights of waves 0 .. v - 1
+  __device__ int64_t cum_weight(int v) const {
+    return 64 * static_cast<int64_t>((v + 1) / 2) + static_cast<int64_t>(wo) * (v / 2);
+  }
 
   // floor(n / d) for 0 <= n < 2^53 and 0 < d < 2^31: a double estimate (off by at most one
   // for these sizes), corrected with exact integer products
@@ -573,10 +588,15 @@ struct Work {
     Wp = min(a.num_waves, total);
     if (T == 0 || w >= Wp) return;
     inv_total = 1.0 / static_cast<double>(total);
-    const double inv_wp = 1.0 / static_cast<double>(Wp);
-    const int th0 = static_cast<int>(div_floor(static_cast<int64_t>(w) * total + Wp - 1, Wp, inv_wp));
-    const int th1 =
-        w + 1 == Wp ? total : static_cast<int>(div_floor(static_cast<int64_t>(w + 1) * total + Wp - 1, Wp, inv_wp));
+    // wave w takes positions [th(w), th(w + 1)), th(v) = ceil(cum_weight(v) total / Om).  With
+    // total >= 2 Wp every share is at least one position wide (an odd wave's is at least
+    // floor(2 wo / 64) >= 1), so every wave in a segment's {first, last} range holds a piece
+    // of it; smaller batches take equal weights.
+    wo = total >= 2 * Wp ? kOddDieWeight : 64;
+    Om = cum_weight(Wp);
+    inv_om = 1.0 / static_cast<double>(Om);
+    const int th0 = static_cast<int>(div_floor(cum_weight(w) * total + Om - 1, Om, inv_om));
+    const int th1 = w + 1 == Wp ? total : static_cast<int>(div_floor(cum_weight(w + 1) * total + Om - 1, Om, inv_om));
     // the first tiles at positions >= th0 and >= th1 (th1 = total: none, the end); with
     // partitions, the first tiles of the first partitions there
     int x0 = -1, x1 = T;
@@ -633,10 +653,14 @@ struct Work {
     n_my = x0 < 0 ? 0 : x1 - x0;
   }
 
-  // the wave holding the last tile of c's segment (default split)
+  // the wave holding the last tile of c's segment (default split): the last wave v with
+  // th(v) <= p, i.e. cum_weight(v) <= X = floor(p Om / total); waves 2k and 2k + 1 start at
+  // weights k (64 + wo) and k (64 + wo) + 64
   __device__ int wave_of_last(const Cursor& c) const {
     const int p = c.gstart + c.nt - 1 + c.seg + 1;
-    return static_cast<int>(div_floor(static_cast<int64_t>(p) * Wp, total, inv_total));
+    const int X = static_cast<int>(div_floor(static_cast<int64_t>(p) * Om, total, inv_total));
+    const int k = X / (64 + wo);
+    return min(2 * k + (X - k * (64 + wo) >= 64 ? 1 : 0), Wp - 1);
   }
 
   __device__ void advance(Cursor& c) const {
