@@ -3391,12 +3391,14 @@ int check_decode(const DecodeCall& c, Geom* g, bool need_ws = true) {
   if (c.num_q_heads > 65535) return fail(PA_ERR_INVALID_ARG, "num_q_heads %d > 65535", c.num_q_heads);
   *g = geometry(c.num_seqs, c.num_q_heads, c.num_kv_heads, c.head_dim, c.max_context_len, c.partition_size,
                 c.dtype);
-  // tile counts, segment indexes and the work split's cost positions (tiles plus segments)
+  // tile counts, segment indexes and the work split's cost positions (tiles plus pieces)
   // are 32-bit in the kernels (a tile holds at least 8 tokens; every segment counts once
-  // besides, since the split and the reduce count all of them)
-  if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((static_cast<int64_t>(c.max_context_len) + 7) / 8 + 1) >
-      (static_cast<int64_t>(1) << 31) - 1)
-    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles or segments");
+  // besides, or once per partition with fixed partitions, since the split and the reduce
+  // count all of them)
+  const int64_t mcl = c.max_context_len;
+  const int64_t pieces = c.partition_size > 0 ? std::max<int64_t>(1, (mcl + c.partition_size - 1) / c.partition_size) : 1;
+  if (static_cast<int64_t>(c.num_seqs) * g->n_units * ((mcl + 7) / 8 + pieces) > (static_cast<int64_t>(1) << 31) - 1)
+    return fail(PA_ERR_INVALID_ARG, "batch too large: more than 2^31 - 1 tiles and pieces");
   if (g->rec_cap * g->rec_rows > (static_cast<int64_t>(1) << 31) - 1)  // record rows are 32-bit indexes
     return fail(PA_ERR_INVALID_ARG, "too many partitions: %lld records of %d rows", (long long)g->rec_cap,
                 g->rec_rows);

@@ -112,6 +112,16 @@ def test_decode_rejects_bad_arguments(over, code):
     assert P.last_error() != ""
 
 
+def test_decode_counts_every_partition_in_the_split_bound():
+    # 1.5e9-token contexts at fp32 (8-token tiles): the default split's cost (tiles plus one
+    # per segment) fits in 32 bits, 16-token partitions (one more per partition) do not
+    big = dict(S=1, hkv=8, hq=32, mcl=1_500_000_000, mb=1_500_000_000 // 16, dt=_lib.PA_F32, wsb=1 << 62)
+    assert _decode(P=16, **big) == _lib.PA_ERR_INVALID_ARG
+    assert "tiles and pieces" in P.last_error()
+    _decode(P=0, **big)  # fails later, on the fake workspace pointer, not on the bound
+    assert "tiles and pieces" not in P.last_error()
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert _decode(S=0, out=None, q=None) == _lib.PA_OK
     assert P.last_error() == ""
