@@ -137,7 +137,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
  * scale              softmax scale (1/sqrt(head_dim) on the pages); positive and finite
  * max_context_len    host bound on every context_lens[s]; at most max_blocks_per_seq * block_size
  * num_seqs, num_q_heads  at most 65535 each (grid dimensions); num_seqs * num_kv_heads at
- *                    most 2^31 - 1 segments, and at most 2^31 - 1 tiles of 8 tokens in all
+ *                    most 2^31 - 1 segments, and, counting max_context_len for every
+ *                    segment, at most 2^31 - 1 tiles of 8 tokens plus pieces (one per
+ *                    segment, or one per partition) in all
+ * partition_size     0 (the default split) or a positive multiple of 16 and of block_size
+ *                    (fixed partitions); see the work split above
  * workspace          device, >= pa_decode_workspace_bytes(...) bytes, 256-byte aligned;
  *                    contents need no initialisation and are scratch between calls
  *
