@@ -156,6 +156,13 @@ def _dtype_code(t) -> int:
     raise PaError("binding", PA_ERR_UNSUPPORTED, f"dtype {t.dtype} is not float16 or float32")
 
 
+def _same_dtype(call, *tensors):
+    """One element type for all of them: the C ABI takes one dtype code for the call."""
+    kinds = {t.dtype for t in tensors}
+    if len(kinds) > 1:
+        raise PaError(call, PA_ERR_INVALID_ARG, f"mixed element types {sorted(str(k) for k in kinds)}")
+
+
 def _ptr(t) -> int:
     if not t.is_contiguous():
         raise PaError("binding", PA_ERR_INVALID_ARG, "tensors must be contiguous")
@@ -172,6 +179,7 @@ def _stream(t, stream) -> int:
 def pa_cache_write(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     """k_cache[slot // B, :, slot % B] = k[t] (same for v) for every t with slot >= 0."""
     num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    _same_dtype("pa_cache_write", k, v, k_cache, v_cache)
     code = lib().pa_cache_write(
         _ptr(k), _ptr(v), _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), k.shape[0],
         num_kv_heads, head_dim, block_size, num_blocks, _dtype_code(k_cache),
@@ -186,8 +194,9 @@ def pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
-                 num_kv_heads, max_context_len, partition_size, workspace, stream):
+                 num_kv_heads, max_context_len, partition_size, workspace, stream, pools_like_q=True):
     import torch
+    _same_dtype("pa_decode", out, q, *((k_cache, v_cache) if pools_like_q else ()))
     num_seqs, num_q_heads, head_dim = q.shape
     num_blocks = k_cache.shape[0]
     max_blocks = block_tables.shape[1]
@@ -224,6 +233,7 @@ def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scal
                       stream=None) -> None:
     """pa_decode with no workspace: the library's static scratch serves as one, and nothing
     is allocated (neither here nor in the library)."""
+    _same_dtype("pa_decode_noalloc", out, q, k_cache, v_cache)
     num_seqs, num_q_heads, head_dim = q.shape
     max_blocks = block_tables.shape[1]
     if max_context_len is None:
@@ -374,7 +384,7 @@ def _decode_fp8_args(out, q, k_cache, v_cache, block_tables, context_lens, scale
     _require_codes(v_cache, "v_cache")
     args, workspace = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale,
                                    block_size, num_kv_heads, max_context_len, partition_size,
-                                   workspace, stream)
+                                   workspace, stream, pools_like_q=False)
     if args[16] != PA_F16:
         raise PaError("binding", PA_ERR_UNSUPPORTED, "q and out must be float16 with E4M3 pools")
     # (out, q, kc, vc, bt, ctx, scale, k_scale, v_scale, block_size, ...) without the dtype

@@ -122,6 +122,26 @@ def test_decode_counts_every_partition_in_the_split_bound():
     assert "tiles and pieces" not in P.last_error()
 
 
+def test_other_element_types_are_refused():
+    assert _decode(dt=2) == _lib.PA_ERR_UNSUPPORTED
+    assert "dtype" in P.last_error()
+    assert P.lib().pa_cache_write(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 128, 16, 100, 2, None) == \
+        _lib.PA_ERR_UNSUPPORTED
+
+
+def test_binding_refuses_mixed_element_types():
+    import torch
+    q = torch.zeros((2, 8, 64), dtype=torch.bfloat16)
+    kc = torch.zeros((4, 2, 16, 64), dtype=torch.float16)
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    ctx = torch.ones((2,), dtype=torch.int32)
+    with pytest.raises(P.PaError, match="mixed element types"):
+        P.pa_decode(torch.empty_like(q), q, kc, kc, bt, ctx, 0.1, 16, 2, max_context_len=64)
+    k = torch.zeros((3, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(P.PaError, match="mixed element types"):
+        P.pa_cache_write(k, k, torch.zeros(3, dtype=torch.int64), kc, kc)
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert _decode(S=0, out=None, q=None) == _lib.PA_OK
     assert P.last_error() == ""
