@@ -319,6 +319,24 @@ def test_physical_permutation_bit_identical():
     assert got.tobytes() == ref.tobytes()
 
 
+@pytest.mark.parametrize("partition", [512, 64])
+def test_fixed_partitions_are_independent_of_the_batch(partition):
+    """With fixed partitions an E4M3 row is bitwise the same alone, duplicated or reordered."""
+    torch = _torch()
+    case = _mid_case()
+    ks, vs = _scales(case)
+    d = _to_device(case, ks, vs)
+    full = _decode(case, d, ks, vs, partition_size=partition)
+    rows = [5, 0, 5, 3, 4]
+    idx = torch.tensor(rows, device="cuda")
+    sub = type("D", (), {})()
+    sub.q, sub.tables, sub.ctx = d.q[idx].contiguous(), d.tables[idx].contiguous(), d.ctx[idx].contiguous()
+    sub.k_cache, sub.v_cache = d.k_cache, d.v_cache
+    got = _decode(case, sub, ks, vs, partition_size=partition)
+    for j, s in enumerate(rows):
+        assert got[j].tobytes() == full[s].tobytes(), f"P{partition}: batch row {j} (seq {s})"
+
+
 def test_split_launches_equal_single_call():
     case = _mid_case()
     ks, vs = _scales(case)
