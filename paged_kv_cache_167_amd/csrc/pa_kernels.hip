@@ -74,8 +74,10 @@ constexpr int kF8Stages = 2;      // with a shallower ring keep more loads in fl
 // One-wave work-groups go to the eight dies in turn, so wave w runs on die w mod 8.  The
 // odd-numbered dies of MI355X stream K/V 4-8 % slower than the even ones (measured per die on
 // several boards), so the stream kernels give an odd-numbered wave a share of this weight
-// (of 64) against an even one's.
+// (of 64) against an even one's -- on a whole device (all kWholeDeviceCUs compute units, eight
+// dies); a partitioned one keeps equal weights.
 constexpr int kOddDieWeight = 60;
+constexpr int kWholeDeviceCUs = 256;
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -448,6 +450,7 @@ struct StreamArgs {
   float* rec_l;         // [records * rec_rows] exp-sum per row
   float* rec_o;         // [records * rec_rows * D] normalised output per row
   int part_tiles;       // > 0: pieces are fixed partitions of this many tiles (one record each)
+  int odd_weight;       // share weight (of 64) of an odd-numbered wave: kOddDieWeight or 64
   const void* q;
   const void* k_cache;
   const void* v_cache;
@@ -592,7 +595,7 @@ struct Work {
     // total >= 2 Wp every share is at least one position wide (an odd wave's is at least
     // floor(2 wo / 64) >= 1), so every wave in a segment's {first, last} range holds a piece
     // of it; smaller batches take equal weights.
-    wo = total >= 2 * Wp ? kOddDieWeight : 64;
+    wo = total >= 2 * Wp ? a.odd_weight : 64;
     Om = cum_weight(Wp);
     inv_om = 1.0 / static_cast<double>(Om);
     const int th0 = static_cast<int>(div_floor(cum_weight(w) * total + Om - 1, Om, inv_om));
@@ -3492,6 +3495,9 @@ Residency residency(const void* kernel) {
   return r;
 }
 
+// The odd-numbered waves' share weight: kOddDieWeight on a whole device, else equal weights.
+int die_weight(const void* kernel) { return residency(kernel).cus == kWholeDeviceCUs ? kOddDieWeight : 64; }
+
 // Waves of one launch: `base`, never more than the workspace allows.
 int waves_for(const DecodeCall&, const Geom& g, int64_t base) {
   int64_t w = base > 0 ? base : kMaxWaves;
@@ -3551,6 +3557,7 @@ StreamArgs stream_args(const DecodeCall& c, const Geom& g) {
   a.num_waves = 1;
   a.rec_rows = g.rec_rows;
   a.part_tiles = 0;  // set by the launch, from its kernel's tile
+  a.odd_weight = 64;  // set by the launch, from the device
   a.dense_k = a.dense_v = a.guard_k = a.guard_v = nullptr;
   a.seq_bytes = a.token_bytes = 0;
   if (c.dense) {
@@ -3573,6 +3580,7 @@ int launch_stream(const DecodeCall& c, const Geom& g) {
   StreamArgs a = stream_args(c, g);
   a.part_tiles = c.partition_size / Cfg<T, D, GT>::kTK;  // a multiple of 16 tokens: whole tiles
   a.num_waves = waves_valu<T, D, GT>(c, g);
+  a.odd_weight = die_weight(reinterpret_cast<const void*>(pa_stream_kernel<T, D, GT>));
   if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_kernel failed");
   hipLaunchKernelGGL((pa_stream_kernel<T, D, GT>), dim3(a.num_waves), dim3(kWave), 0, c.stream, a);
   return check_hip("pa_stream_kernel launch");
@@ -3584,6 +3592,7 @@ int launch_stream_mfma(const DecodeCall& c, const Geom& g, int waves_per_cu) {
   StreamArgs a = stream_args(c, g);
   a.part_tiles = c.partition_size / MCfg<D, F8>::kTK;  // a multiple of 16 tokens: whole tiles
   a.num_waves = waves_mfma<D, NST, F8, DENSE, APPEND>(c, g, waves_per_cu);
+  a.odd_weight = die_weight(reinterpret_cast<const void*>(pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>));
   if (a.num_waves <= 0) return fail(PA_ERR_HIP, "occupancy query for pa_stream_mfma_kernel failed");
   hipLaunchKernelGGL((pa_stream_mfma_kernel<D, NST, F8, DENSE, APPEND>), dim3(a.num_waves), dim3(kWave), 0, c.stream,
                      a);
