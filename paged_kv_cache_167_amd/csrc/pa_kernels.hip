@@ -3,8 +3,8 @@
 // Three kernels:
 //   pa_cache_write_kernel  -- scatter each new token's K/V row into its slot.
 //   pa_stream_kernel       -- attention over the paged K/V, the whole batch streamed
-//                             by persistent waves that each own an equal share of it
-//                             (equal in tiles plus piece boundaries).
+//                             by persistent waves that each own a share of it (equal
+//                             in tiles plus piece boundaries, weighted by die).
 //   pa_reduce_kernel       -- log-sum-exp merge of the pieces a context was split into.
 //
 // Sources (page title, section):
@@ -903,7 +903,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
       for (int e = 0; e < DL; ++e) acc[g][e] = 0.0f;
     }
     piece_bad = false;
-    if (cc.t == 0 && lane == 0)  // this wave starts the segment: record who holds its pieces
+    if (cc.t == 0 && lane == 0)  // this wave starts the segment: where its pieces are (waves, or partitions)
       a.seg_desc[cc.s * a.n_units + cc.unit] =
           a.part_tiles > 0 ? make_int2(cc.p0, wk.parts_of(cc.nt)) : make_int2(w, wk.wave_of_last(cc));
     // Wait for the q rows here, once per piece.  Left to the compiler, the wait lands at
@@ -1003,8 +1003,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_kernel(const StreamArgs a) {
     merge_state(g, as_f(mx[1]), as_f(lx[1]), hi_acc);
   };
 
-  // finish the piece that ends with the current tile: merge the token groups, then
-  // write the rows (whole segment) or a piece record (segment shared with other waves)
+  // finish the piece that ends with the current tile: merge the token groups, then write
+  // the rows (a segment this wave holds whole, or of one partition) or a piece record
   auto piece_end = [&]() {
 #pragma unroll
     for (int g = 0; g < GT; ++g) {
@@ -1768,7 +1768,7 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
     m = -INFINITY;
     l = 0.0f;
     piece_bad = false;
-    if (cc.t == 0 && lane == 0)  // who holds the segment's pieces
+    if (cc.t == 0 && lane == 0)  // where the segment's pieces are: its waves, or its partitions
       a.seg_desc[cc.s * a.n_units + cc.unit] =
           a.part_tiles > 0 ? make_int2(cc.p0, wk.parts_of(cc.nt)) : make_int2(w, wk.wave_of_last(cc));
   };
@@ -1829,7 +1829,8 @@ __global__ __launch_bounds__(kWave) void pa_stream_mfma_kernel(const StreamArgs 
   };
 
   // finish the piece that ends with the current tile: the row's exp-sum over its four
-  // lanes, then the rows (whole segment) or a piece record (segment shared with others)
+  // lanes, then the rows (a segment this wave holds whole, or of one partition) or a piece
+  // record
   auto piece_end = [&]() __attribute__((always_inline)) {
     float lt = l;
     {
@@ -3180,8 +3181,9 @@ __global__ __launch_bounds__(kPfWaves * kWave, 2) void pa_prefill_kernel(const P
 // ---------------------------------------------------------------------------
 // decode, second launch (of every decode call, or pa_decode_reduce alone): one wave per
 // (sequence, query head).  Empty or invalid contexts get their zero or NaN row
-// here; a segment held whole by one wave was written by it; a segment split over waves
-// w0..w1 is merged from the tail record of w0 and the head records of w0+1..w1.
+// here; a segment held whole by one wave (or of one partition) was written by it; a
+// segment split over waves w0..w1 is merged from the tail record of w0 and the head
+// records of w0+1..w1, and one cut into fixed partitions from its partitions' records.
 // ---------------------------------------------------------------------------
 
 template <typename T, int D, int GT>
